@@ -1,0 +1,227 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer step library.
+ *
+ * The library applies one optimizer step to tensors the caller owns (for
+ * example PyTorch-allocated device memory), asynchronously on the caller's
+ * HIP stream.  Three calls make up the hot path:
+ *
+ *   muon_init           -- bind a handle to a gfx950 device;
+ *   muon_step_batched   -- one Muon step over a list of 2D weight matrices;
+ *   adamw_step          -- one fused AdamW step over a list of tensors.
+ *
+ * What the Muon step computes, per matrix W of shape (rows, cols) =
+ * (fan-out, fan-in), gradient G and momentum M ("About Muon: Why Not Adam",
+ * kiungsong.github.io, section "The whole thing, in about forty lines", with
+ * the lemma and coefficients of section "Making It Actually Run"):
+ *
+ *   M <- mu*M + (1-mu)*G                          momentum (moving average)
+ *   Y <- (1-mu)*G + mu*M   (Y <- M if !nesterov)  Nesterov blend, updated M
+ *   X <- Y / (||Y||_F + eps)                      singular values into (0,1]
+ *   if rows > cols: X <- X^T                      Gram on the short side
+ *   repeat ns_steps times:                        quintic Newton-Schulz
+ *       A <- X X^T;  B <- b*A + c*A*A;  X <- a*X + B*X
+ *   O <- X (transposed back if it was transposed)
+ *   W <- (1 - lr*weight_decay)*W                  decoupled weight decay
+ *   W <- W - lr*s*O    s = shape multiplier * extra_scale
+ *
+ * with (a,b,c) = (3.4445, -4.7750, 2.0315) every iteration unless the caller
+ * passes its own table ("The Optimizer Wars: How Muon Is Replacing Adam in
+ * Frontier AI Training", ai.info, section "What is Muon? ...").
+ *
+ * Threading: a handle may be used by one host thread at a time.  Calls only
+ * enqueue work (plus, in muon_step_batched, a small host-to-device copy of
+ * the descriptor table from pinned memory the handle owns) and return; they
+ * never wait for the device except to recycle one of the handle's pinned
+ * descriptor slots (at most 8 calls in flight per handle).
+ *
+ * Errors: every call validates all of its arguments before it enqueues
+ * anything.  Any status other than MUON_ERR_HIP means nothing was enqueued.
+ * No call aborts, throws or prints.  Non-finite input values are not
+ * checked: they propagate into the outputs as IEEE arithmetic dictates.
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARG = 1,        /* null pointer, bad size/stride/enum  */
+    MUON_ERR_UNSUPPORTED_DEVICE = 2, /* not a gfx950 device, or bad ordinal */
+    MUON_ERR_WORKSPACE = 3,          /* workspace null or smaller than required */
+    MUON_ERR_OVERLAP = 4,            /* param/grad/momentum ranges overlap  */
+    MUON_ERR_HIP = 5,                /* a HIP runtime call failed           */
+    MUON_ERR_UNALIGNED = 6           /* pointer not aligned to its element  */
+} muon_status;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* Per-matrix multiplier of the orthogonalised update
+ * ("About Muon: Why Not Adam", sections "Why Muon?" and "How Do We Turn It
+ * Into a Real Optimizer?"):
+ *   MOONLIGHT  0.2*sqrt(max(rows, cols))  (entry RMS ~0.2; shares AdamW's lr)
+ *   JORDAN     sqrt(max(1, rows/cols))
+ *   BERNSTEIN  sqrt(rows/cols)            (sqrt(fan-out/fan-in))
+ *   NONE       1
+ * The result is multiplied by muon_hparams.extra_scale. */
+typedef enum {
+    MUON_SCALE_MOONLIGHT = 0,
+    MUON_SCALE_JORDAN = 1,
+    MUON_SCALE_BERNSTEIN = 2,
+    MUON_SCALE_NONE = 3
+} muon_scale_mode;
+
+typedef struct muon_context* muon_handle;
+
+/* One Muon matrix.  All pointers are device pointers owned by the caller.
+ * Layout is row-major (rows, cols) with leading dimensions in elements
+ * (ld >= cols).  A row block of a fused tensor (e.g. Q, K and V of a fused
+ * QKV weight, "Why Muon Works", section 7.3) is passed as its own matrix
+ * with offset pointers.
+ *   param      W, F32 or BF16, updated in place.
+ *   grad       G, F32 or BF16, read only.
+ *   momentum   M, always F32, updated in place (caller zero-fills it before
+ *              the first step).
+ *   update_out optional (NULL = skip): dense rows x cols F32 array that
+ *              receives O, the orthogonalised update before the multiplier.
+ *   norm_out   optional (NULL = skip): one F32 that receives ||Y||_F. */
+typedef struct {
+    void* param;
+    const void* grad;
+    float* momentum;
+    float* update_out;
+    float* norm_out;
+    int64_t rows, cols;
+    int64_t ld_param, ld_grad, ld_mom;
+    int32_t param_dtype; /* muon_dtype */
+    int32_t grad_dtype;  /* muon_dtype */
+} muon_matrix;
+
+/* Step hyperparameters, shared by every matrix of one call.
+ *   coeffs: NULL = (3.4445, -4.7750, 2.0315) for every iteration; otherwise a
+ *           HOST array of 3*ns_steps floats (a, b, c per iteration), read
+ *           during the call only.
+ *   ns_dtype: MUON_BF16 (bf16 operands, fp32 accumulation) or MUON_F32. */
+typedef struct {
+    float lr;
+    float momentum;     /* mu, typically 0.95 */
+    float weight_decay;
+    float eps;          /* added to ||Y||_F, typically 1e-7 */
+    float extra_scale;  /* typically 1 */
+    int32_t nesterov;   /* 1 = Nesterov blend (default), 0 = plain momentum */
+    int32_t ns_steps;   /* >= 1, typically 5 */
+    int32_t ns_dtype;   /* muon_dtype */
+    int32_t scale_mode; /* muon_scale_mode */
+    const float* coeffs;
+} muon_hparams;
+
+/* One AdamW tensor (flat, numel elements, contiguous).  param F32 or BF16;
+ * grad F32 or BF16; exp_avg and exp_avg_sq F32.  Device pointers, caller
+ * owned, updated in place. */
+typedef struct {
+    void* param;
+    const void* grad;
+    float* exp_avg;
+    float* exp_avg_sq;
+    int64_t numel;
+    int32_t param_dtype;
+    int32_t grad_dtype;
+} adamw_tensor;
+
+/* AdamW hyperparameters ("Por qué AdamW para entrenar modelos de lenguaje,
+ * y qué está cambiando", gustavoai.dev, sections "Adam: las dos ideas
+ * juntas", "La W: ..." and "Por qué AdamW, y por qué con esos números").
+ *   step: t >= 1, already incremented by the caller (bias correction uses
+ *         1 - beta^t). */
+typedef struct {
+    float lr;
+    float beta1;        /* 0.9  */
+    float beta2;        /* 0.95 */
+    float eps;          /* 1e-8, added to sqrt(v_hat) */
+    float weight_decay; /* 0.1, decoupled: theta -= lr*wd*theta_old */
+    int64_t step;
+} adamw_hparams;
+
+/* Bind a handle to HIP device `device`.  Fails with
+ * MUON_ERR_UNSUPPORTED_DEVICE unless the device is gfx950.  Allocates the
+ * handle's pinned host descriptor slots.  Release with muon_destroy. */
+muon_status muon_init(int device, muon_handle* out);
+
+/* Free the handle (waits for the handle's pending descriptor copies). */
+muon_status muon_destroy(muon_handle h);
+
+/* Bytes of device workspace muon_step_batched needs for exactly these
+ * matrices and hyperparameters (shapes and ns_dtype matter; pointers don't).
+ * Same validation as muon_step_batched except for the pointers. */
+muon_status muon_workspace_size(muon_handle h, const muon_matrix* mats, int n,
+                                const muon_hparams* hp, size_t* bytes);
+
+/* One Muon step over n matrices on `stream` (a hipStream_t; NULL = the
+ * device's null stream).  `workspace` is caller-owned device memory of at
+ * least muon_workspace_size bytes, 256-byte aligned, used only by this call's
+ * kernels; it must not be shared by calls that may run concurrently.  The
+ * descriptor array is host memory, read during the call only.  Rejects:
+ * n < 1, rows or cols < 1, ld < cols, a null param/grad/momentum, an unknown
+ * dtype or mode, ns_steps < 1, lr/momentum non-finite, overlapping
+ * param/grad/momentum ranges within a matrix, a small or null workspace. */
+muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
+                              const muon_hparams* hp, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* One AdamW step over n tensors on `stream`.  No workspace: the tensor list
+ * travels in kernel arguments (groups of at most 32 tensors per launch).
+ * Rejects n < 1, numel < 0, null pointers for numel > 0, unknown dtypes,
+ * step < 1. */
+muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n,
+                       const adamw_hparams* hp, void* stream);
+
+/* ---- per-phase timing (benchmarks) ---------------------------------------
+ * While enabled, muon_step_batched records a pair of HIP events (on the
+ * caller's stream) around every kernel launch it makes, and adamw_step around
+ * each of its launches.  muon_profile_collect waits for the last recorded
+ * event, adds up the elapsed times per phase since the previous collect (or
+ * enable), fills `out` and clears the record.  Timing does not change what the
+ * kernels compute.  Phases: 0 momentum, 1 norm, 2 gram, 3 poly, 4 update,
+ * 5 apply, 6 adamw. */
+#define MUON_NUM_PHASES 7
+typedef struct {
+    float ms[MUON_NUM_PHASES];     /* summed launch durations per phase */
+    int32_t launches[MUON_NUM_PHASES];
+} muon_phase_times;
+
+muon_status muon_profile_enable(muon_handle h, int enable);
+muon_status muon_profile_collect(muon_handle h, muon_phase_times* out);
+
+/* Static, human readable name of a status. */
+const char* muon_status_str(muon_status s);
+
+/* ---- single-phase entry points (test hooks) ------------------------------
+ * Each runs one phase of the Newton-Schulz iteration on bf16 device buffers
+ * that the caller lays out exactly as muon_step_batched's workspace does:
+ * m x n row-major with leading dimension ld (elements), m and n multiples of
+ * 256 and every element outside the valid region zero.  They exist so that
+ * tests can compare each GEMM against the oracle's intermediate on the same
+ * input.
+ *   gram:   A = s2 * X X^T          (X: m x n, A: m x m)
+ *   poly:   B = b*A + c*A A         (A, B: m x m, A symmetric)
+ *   update: Xo = s*(a*X + B X), XoT = Xo^T  (X: m x n; XoT: n x m)
+ */
+muon_status muon_test_gram_bf16(muon_handle h, const void* X, void* A, int64_t m,
+                                int64_t n, int64_t ldx, int64_t lda, float s2, void* stream);
+muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m,
+                                int64_t lda, float b, float c, void* stream);
+muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* XT,
+                                  const void* B, void* Xo, void* XoT, int64_t m,
+                                  int64_t n, int64_t ldx, int64_t ldb, float a,
+                                  float s, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_MI355X_H */

@@ -1,0 +1,367 @@
+// Memory-bound kernels of the Muon step and the AdamW fallback (gfx950).
+//
+//   momentum_kernel  M <- mu M + (1-mu) G; Y <- Nesterov blend; per-tile
+//                    sum of Y^2; Y written (unnormalised) in both the
+//                    natural and the transposed orientation of the padded
+//                    Newton-Schulz buffers, with zeros in the padding.
+//   norm_finalize    ||Y||_F from the per-tile partial sums (fixed order, so
+//                    every run gives the same bits) and s = 1/(||Y||_F + eps).
+//   apply_kernel     W <- (1 - lr wd) W - lr scale O.
+//   adamw_kernel     fused AdamW over a group of tensors.
+//
+// "About Muon: Why Not Adam" (kiungsong.github.io), section "The whole thing,
+// in about forty lines": the momentum buffer is interpolated towards the
+// gradient by 1 - mu, the Nesterov input interpolates the gradient towards
+// the updated buffer by mu, the iteration starts from Y / (||Y||_F + eps),
+// and the weight is decayed by (1 - lr wd) before the scaled update is
+// subtracted.  AdamW: "Por qué AdamW para entrenar modelos de lenguaje, y qué
+// está cambiando" (gustavoai.dev), sections "Adam: las dos ideas juntas" and
+// "La W: un error de regularización que duró tres años".
+//
+// Each workgroup of the Muon kernels owns one 64 x 64 tile of one weight;
+// 256 threads, each thread four rows of four consecutive columns, so a wave
+// reads four 256-byte row segments per instruction (fp32).
+#include "muon_internal.h"
+
+namespace muon {
+
+namespace {
+
+struct Vals4 {
+    float v[4];
+};
+
+template <bool VEC>
+__device__ __forceinline__ Vals4 load4(const void* base, int dtype_bf16, int64_t off, int valid) {
+    Vals4 r;
+    if (VEC) {
+        if (dtype_bf16) {
+            uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+            r.v[0] = __builtin_bit_cast(float, u.x << 16);
+            r.v[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+            r.v[2] = __builtin_bit_cast(float, u.y << 16);
+            r.v[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+        } else {
+            float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+            r.v[0] = f.x; r.v[1] = f.y; r.v[2] = f.z; r.v[3] = f.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < valid) {
+                r.v[e] = dtype_bf16
+                    ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[off + e])
+                    : reinterpret_cast<const float*>(base)[off + e];
+            } else {
+                r.v[e] = 0.f;
+            }
+        }
+    }
+    return r;
+}
+
+template <bool VEC>
+__device__ __forceinline__ void store4(void* base, int dtype_bf16, int64_t off, const Vals4& r,
+                                       int valid) {
+    if (VEC) {
+        if (dtype_bf16) {
+            uint2 u;
+            u.x = (uint32_t)f32_to_bf16_bits(r.v[0]) | ((uint32_t)f32_to_bf16_bits(r.v[1]) << 16);
+            u.y = (uint32_t)f32_to_bf16_bits(r.v[2]) | ((uint32_t)f32_to_bf16_bits(r.v[3]) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = u;
+        } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) =
+                make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < valid) {
+                if (dtype_bf16)
+                    reinterpret_cast<uint16_t*>(base)[off + e] = f32_to_bf16_bits(r.v[e]);
+                else
+                    reinterpret_cast<float*>(base)[off + e] = r.v[e];
+            }
+        }
+    }
+}
+
+// Store four values into a Newton-Schulz buffer (bf16 or f32), 4-aligned.
+template <bool NS_F32>
+__device__ __forceinline__ void store_ns4(void* base, int64_t off, const float* v) {
+    if (NS_F32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) =
+            make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        uint2 u;
+        u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = u;
+    }
+}
+
+template <bool NS_F32>
+__device__ __forceinline__ void load_ns4(const void* base, int64_t off, float* v) {
+    if (NS_F32) {
+        float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
+        uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+        v[0] = __builtin_bit_cast(float, u.x << 16);
+        v[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+        v[2] = __builtin_bit_cast(float, u.y << 16);
+        v[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    if (threadIdx.x == 0) t = (red[0] + red[1]) + (red[2] + red[3]);
+    return t;
+}
+
+template <bool VEC, bool NS_F32>
+__device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu, int nesterov,
+                                              float (*tileT)[kEwTile + 1], float* red) {
+    const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
+    const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
+    const int t = threadIdx.x;
+    const int cg = (t & 15) * 4;
+    const int rr = t >> 4;
+    const int64_t rows = d.rows, cols = d.cols;
+    const int gbf = d.grad_dtype == MUON_BF16;
+    // natural orientation (rows_pad x cols_pad, ld cols_pad) and transposed
+    // orientation (cols_pad x rows_pad, ld rows_pad) of Y
+    void* nat = d.transposed ? d.xt[0] : d.x[0];
+    void* trn = d.transposed ? d.x[0] : d.xt[0];
+    const int64_t ld_nat = d.cols_pad, ld_trn = d.rows_pad;
+    const float omm = 1.f - mu;
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int lr = rr + 16 * q;
+        const int64_t r = r0 + lr;
+        const int64_t c = c0 + cg;
+        float y[4] = {0.f, 0.f, 0.f, 0.f};
+        const int64_t cv = cols - c;
+        const int valid = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
+        if (valid > 0) {
+            Vals4 g = load4<VEC>(d.grad, gbf, r * d.ld_grad + c, valid);
+            Vals4 m = load4<VEC>(d.mom, 0, r * d.ld_mom + c, valid);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float mn = mu * m.v[e] + omm * g.v[e];
+                m.v[e] = mn;
+                const float yy = nesterov ? (omm * g.v[e] + mu * mn) : mn;
+                y[e] = (e < valid) ? yy : 0.f;
+                ss += y[e] * y[e];
+            }
+            store4<VEC>(d.mom, 0, r * d.ld_mom + c, m, valid);
+        }
+        store_ns4<NS_F32>(nat, r * ld_nat + c, y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tileT[cg + e][lr] = y[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int lc = rr + 16 * q;  // column of the weight = row of Y^T
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = tileT[lc][cg + e];
+        store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cg, v);
+    }
+    const float tot = block_sum_256(ss, red);
+    if (threadIdx.x == 0) d.partials[lt] = tot;
+}
+
+template <bool NS_F32>
+__global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ descs, int n,
+                                                       const int32_t* __restrict__ prefix,
+                                                       float mu, int nesterov) {
+    __shared__ float tileT[kEwTile][kEwTile + 1];
+    __shared__ float red[4];
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    const MatDesc& d = descs[mi];
+    const int lt = tile - prefix[mi];
+    if (d.vec4)
+        momentum_tile<true, NS_F32>(d, lt, mu, nesterov, tileT, red);
+    else
+        momentum_tile<false, NS_F32>(d, lt, mu, nesterov, tileT, red);
+}
+
+__global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
+                                                            float eps) {
+    const MatDesc& d = descs[blockIdx.x];
+    __shared__ double red[4];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < d.ew_tiles; i += 256) s += (double)d.partials[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double tot = (red[0] + red[1]) + (red[2] + red[3]);
+        const double nu = sqrt(tot);
+        d.inv_norm[0] = (float)(1.0 / (nu + (double)eps));
+        if (d.norm_out) d.norm_out[0] = (float)nu;
+    }
+}
+
+template <bool VEC, bool NS_F32>
+__device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity, float decay,
+                                           float step) {
+    const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
+    const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
+    const int t = threadIdx.x;
+    const int cg = (t & 15) * 4;
+    const int rr = t >> 4;
+    const int64_t rows = d.rows, cols = d.cols;
+    const int pbf = d.param_dtype == MUON_BF16;
+    // O in the weight's orientation: X when not transposed, X^T otherwise;
+    // either way rows_pad x cols_pad with ld cols_pad.
+    const void* O = d.transposed ? d.xt[parity] : d.x[parity];
+    const int64_t ld_o = d.cols_pad;
+    const float sc = step * d.scale;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t r = r0 + rr + 16 * q;
+        const int64_t c = c0 + cg;
+        const int64_t cv = cols - c;
+        if (r >= rows || cv <= 0) continue;
+        const int valid = cv >= 4 ? 4 : (int)cv;
+        float o[4];
+        load_ns4<NS_F32>(O, r * ld_o + c, o);
+        Vals4 w = load4<VEC>(d.param, pbf, r * d.ld_param + c, valid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w.v[e] = decay * w.v[e] - sc * o[e];
+        store4<VEC>(d.param, pbf, r * d.ld_param + c, w, valid);
+        if (d.update_out) {
+            Vals4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov.v[e] = o[e];
+            store4<false>(d.update_out, 0, r * cols + c, ov, valid);
+        }
+    }
+}
+
+template <bool NS_F32>
+__global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ descs, int n,
+                                                    const int32_t* __restrict__ prefix,
+                                                    int parity, float decay, float step) {
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    const MatDesc& d = descs[mi];
+    const int lt = tile - prefix[mi];
+    if (d.vec4)
+        apply_tile<true, NS_F32>(d, lt, parity, decay, step);
+    else
+        apply_tile<false, NS_F32>(d, lt, parity, decay, step);
+}
+
+// ---------------------------------------------------------------- AdamW ----
+
+__device__ __forceinline__ void adamw_elem(float& th, float g, float& m, float& v, float lr,
+                                           float b1, float b2, float eps, float wd, float inv_bc1,
+                                           float inv_bc2) {
+    m = b1 * m + (1.f - b1) * g;
+    v = b2 * v + (1.f - b2) * (g * g);
+    const float mhat = m * inv_bc1;
+    const float vhat = v * inv_bc2;
+    th = th - lr * (mhat / (sqrtf(vhat) + eps) + wd * th);
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, float b1, float b2,
+                                                    float eps, float wd, float inv_bc1,
+                                                    float inv_bc2) {
+    const int blk = blockIdx.x;
+    int ti = 0;
+    {
+        int lo = 0, hi = grp.count - 1;
+        while (lo < hi) {
+            int mid = (lo + hi + 1) >> 1;
+            if (grp.block_prefix[mid] <= blk) lo = mid; else hi = mid - 1;
+        }
+        ti = lo;
+    }
+    const int64_t start = (int64_t)(blk - grp.block_prefix[ti]) * kAdamwChunk;
+    const int64_t numel = grp.numel[ti];
+    const int64_t end = start + kAdamwChunk < numel ? start + kAdamwChunk : numel;
+    void* P = grp.param[ti];
+    const void* G = grp.grad[ti];
+    float* M = grp.m[ti];
+    float* V = grp.v[ti];
+    const int pbf = grp.param_bf16[ti], gbf = grp.grad_bf16[ti];
+    if (grp.vec4[ti] && end - start == kAdamwChunk) {
+#pragma unroll
+        for (int q = 0; q < kAdamwChunk / 1024; ++q) {
+            const int64_t off = start + q * 1024 + threadIdx.x * 4;
+            Vals4 th = load4<true>(P, pbf, off, 4);
+            Vals4 g = load4<true>(G, gbf, off, 4);
+            float4 m = *reinterpret_cast<const float4*>(M + off);
+            float4 v = *reinterpret_cast<const float4*>(V + off);
+            adamw_elem(th.v[0], g.v[0], m.x, v.x, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            adamw_elem(th.v[1], g.v[1], m.y, v.y, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            adamw_elem(th.v[2], g.v[2], m.z, v.z, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            adamw_elem(th.v[3], g.v[3], m.w, v.w, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            store4<true>(P, pbf, off, th, 4);
+            *reinterpret_cast<float4*>(M + off) = m;
+            *reinterpret_cast<float4*>(V + off) = v;
+        }
+    } else {
+        for (int64_t i = start + threadIdx.x; i < end; i += 256) {
+            float th = pbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P)[i])
+                           : reinterpret_cast<const float*>(P)[i];
+            const float g = gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
+                                : reinterpret_cast<const float*>(G)[i];
+            float m = M[i], v = V[i];
+            adamw_elem(th, g, m, v, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            if (pbf)
+                reinterpret_cast<uint16_t*>(P)[i] = f32_to_bf16_bits(th);
+            else
+                reinterpret_cast<float*>(P)[i] = th;
+            M[i] = m;
+            V[i] = v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
+                           int nesterov, int ns_f32, hipStream_t st) {
+    if (ns_f32)
+        momentum_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, mu, nesterov);
+    else
+        momentum_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, mu, nesterov);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t st) {
+    norm_finalize_kernel<<<n, 256, 0, st>>>(d, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
+                        float lr, float wd, int ns_f32, hipStream_t st) {
+    const float decay = 1.f - lr * wd;
+    if (ns_f32)
+        apply_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr);
+    else
+        apply_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,
+                        float eps, float wd, float bc1, float bc2, hipStream_t st) {
+    adamw_kernel<<<total_blocks, 256, 0, st>>>(g, lr, beta1, beta2, eps, wd, 1.f / bc1, 1.f / bc2);
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,369 @@
+// bf16 MFMA kernels of the quintic Newton-Schulz iteration (gfx950).
+//
+// One iteration X <- a X + b (X X^T) X + c (X X^T)^2 X is computed on the
+// small Gram as three products ("About Muon: Why Not Adam", kiungsong.github.io,
+// section "Making It Actually Run": the odd polynomial acts on singular values
+// only, and running it on X X^T after the short-side transpose gives the same
+// result):
+//
+//   gram:   A = X X^T                    m' x m', symmetric
+//   poly:   B = b A + c A A              m' x m', symmetric (A A = A A^T)
+//   update: X <- a X + B X               m' x n'
+//
+// All three are "NT" products C[i][j] = sum_k P[i][k] Q[j][k] with both
+// operands read along contiguous rows: X's rows for the Gram, A's rows for
+// the polynomial (A is symmetric), and for the update B's rows and the rows
+// of X^T, which the update itself writes next to X (and the momentum kernel
+// before the first iteration).  Keeping X^T costs one extra bf16 store per
+// element per iteration and turns every operand load into a direct
+// global->LDS copy.
+//
+// The Gram and the polynomial outputs are symmetric: only tiles on or below
+// the diagonal are computed and each off-diagonal tile is stored twice (as
+// itself and mirrored).
+//
+// Tiling: a workgroup computes a BM x BN tile with WM x WN waves, each wave a
+// (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation).  K advances in slabs of 64: operand slabs are copied
+// global->LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
+// staging) into two LDS stages, so the copy of slab k+1 overlaps the MFMAs
+// on slab k.  An LDS row is 64 bf16 = 8 chunks of 16 bytes; chunk c of row r
+// lives at position c ^ (r & 7), so the 32 lanes of a fragment read (32
+// consecutive rows, one chunk) spread over all banks.
+//
+// Grouped launch: one launch per phase covers every matrix; workgroup ->
+// (matrix, tile) through prefix sums of tiles per matrix.
+#include "muon_internal.h"
+
+namespace muon {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+enum { GRAM = 0, POLY = 1, UPDATE = 2 };
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BK = 64;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+    static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 MFMA tile");
+    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "slab rows must split over waves");
+};
+
+// Copy rows [0, R) x k-chunk [0, 64) of a row-major bf16 operand (rows start
+// at `g`, leading dimension ld) into an LDS slab, swizzled.  One
+// global_load_lds_dwordx4 moves 8 rows (1 KB); lane L fills physical chunk
+// L & 7 of row L >> 3, i.e. logical chunk (L & 7) ^ (L >> 3).
+template <int R, int NW>
+__device__ __forceinline__ void load_slab(const uint16_t* __restrict__ g, int64_t ld, uint16_t* slab,
+                                          int wave, int lane) {
+    constexpr int PER_WAVE = (R / 8) / NW;
+    const int lrow = lane >> 3;
+    const int lch = (lane & 7) ^ lrow;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+        const int grp = wave * PER_WAVE + q;
+        const uint16_t* src = g + (int64_t)(grp * 8 + lrow) * ld + lch * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * 8 * 64), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bf16x8 read_frag(const uint16_t* slab, int row, int lch) {
+    const int pch = lch ^ (row & 7);
+    return *reinterpret_cast<const bf16x8*>(slab + row * 64 + pch * 8);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+struct Epi {
+    // output (row-major, ld) and, when `outT` is set, its transpose
+    uint16_t* out;
+    int64_t ld_out;
+    uint16_t* outT;
+    int64_t ld_outT;
+    // term added in the epilogue: coef_e * E[i][j] (E may be null)
+    const uint16_t* E;
+    int64_t ld_e;
+    float coef_e;
+    float coef_acc;  // multiplies the product
+    float post;      // multiplies the sum
+};
+
+// C tile (ti, tj) = sum_k P[i][k] Q[j][k]; P rows start at P0 (tile row 0),
+// Q rows at Q0.  K is a multiple of 64.
+template <class C, bool HAS_E>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64_t ldp,
+                                          const uint16_t* __restrict__ Q0, int64_t ldq, int K,
+                                          int64_t row0, int64_t col0, const Epi& ep, uint16_t* lds) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+
+    f32x16 acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int KT = K / C::BK;
+    // stage s: P slab at lds + s*STAGE, Q slab right after it
+    load_slab<C::BM, C::NW>(P0, ldp, lds, wave, lane);
+    load_slab<C::BN, C::NW>(Q0, ldq, lds + C::BM * C::BK, wave, lane);
+
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
+    for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's slab copies landed
+        __syncthreads();                     // ... and every other wave's
+        const uint16_t* sp = lds + (kt & 1) * C::STAGE;
+        const uint16_t* sq = sp + C::BM * C::BK;
+        if (kt + 1 < KT) {
+            uint16_t* np_ = lds + ((kt + 1) & 1) * C::STAGE;
+            const int64_t k0 = (int64_t)(kt + 1) * C::BK;
+            load_slab<C::BM, C::NW>(P0 + k0, ldp, np_, wave, lane);
+            load_slab<C::BN, C::NW>(Q0 + k0, ldq, np_ + C::BM * C::BK, wave, lane);
+        }
+#pragma unroll
+        for (int kk = 0; kk < C::BK / 16; ++kk) {
+            const int lch = 2 * kk + khalf;
+            bf16x8 a[C::FM], b[C::FN];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) a[i] = read_frag(sp, wm * C::TM + i * 32 + frow, lch);
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) b[j] = read_frag(sq, wn * C::TN + j * 32 + frow, lch);
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // Epilogue.  MFMA 32x32 output layout: lane l, register r holds
+    // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31.  For each row of
+    // fragments the E terms are loaded first (one wait), then combined and
+    // stored.
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        float e[C::FN][16];
+        if (HAS_E) {
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j) {
+                const int64_t col = col0 + wn * C::TN + j * 32 + frow;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t row = row0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                    e[j][r] = bf16_bits_to_f32(ep.E[row * ep.ld_e + col]);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const int64_t col = col0 + wn * C::TN + j * 32 + frow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t rb = row0 + wm * C::TM + i * 32 + 8 * q + 4 * khalf;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = ep.coef_acc * acc[i][j][4 * q + r];
+                    if (HAS_E) x += ep.coef_e * e[j][4 * q + r];
+                    v[r] = ep.post * x;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ep.out[(rb + r) * ep.ld_out + col] = f32_to_bf16_bits(v[r]);
+                if (ep.outT) {
+                    uint2 u;
+                    u.x = pack2(v[0], v[1]);
+                    u.y = pack2(v[2], v[3]);
+                    *reinterpret_cast<uint2*>(ep.outT + col * ep.ld_outT + rb) = u;
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
+    int t = (int)((sqrtf(8.f * (float)lt + 1.f) - 1.f) * 0.5f);
+    while (t * (t + 1) / 2 > lt) --t;
+    while ((t + 1) * (t + 2) / 2 <= lt) ++t;
+    ti = t;
+    tj = lt - t * (t + 1) / 2;
+}
+
+// Gram and polynomial: SYRK-like over the lower triangle of tiles.
+template <class C, int PHASE>
+__global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict__ descs, int n,
+                                                       const int32_t* __restrict__ prefix, int it,
+                                                       float cb, float cc) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    const MatDesc& d = descs[mi];
+    int ti, tj;
+    tri_index(tile - prefix[mi], ti, tj);
+    const int64_t mp = d.mp, np = d.np;
+    Epi ep;
+    ep.out = reinterpret_cast<uint16_t*>(PHASE == GRAM ? d.a : d.b);
+    ep.ld_out = mp;
+    ep.outT = (ti != tj) ? ep.out : nullptr;
+    ep.ld_outT = mp;
+    const uint16_t* src;
+    int64_t ld;
+    if (PHASE == GRAM) {
+        src = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+        ld = np;
+        const float s = (it == 0) ? d.inv_norm[0] : 1.f;
+        ep.E = nullptr;
+        ep.ld_e = 0;
+        ep.coef_e = 0.f;
+        ep.coef_acc = s * s;
+        ep.post = 1.f;
+    } else {
+        src = reinterpret_cast<const uint16_t*>(d.a);
+        ld = mp;
+        ep.E = src;
+        ep.ld_e = mp;
+        ep.coef_e = cb;
+        ep.coef_acc = cc;
+        ep.post = 1.f;
+    }
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, lds);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
+                                                          const int32_t* __restrict__ prefix,
+                                                          int it, float ca) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    const MatDesc& d = descs[mi];
+    const int lt = tile - prefix[mi];
+    const int64_t mp = d.mp, np = d.np;
+    const int tcols = (int)(np / C::BN);
+    const int ti = lt / tcols, tj = lt - ti * tcols;
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
+    const uint16_t* XT = reinterpret_cast<const uint16_t*>(d.xt[it & 1]);
+    Epi ep;
+    ep.out = reinterpret_cast<uint16_t*>(d.x[(it + 1) & 1]);
+    ep.ld_out = np;
+    ep.outT = reinterpret_cast<uint16_t*>(d.xt[(it + 1) & 1]);
+    ep.ld_outT = mp;
+    ep.E = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+    ep.ld_e = np;
+    ep.coef_e = ca;
+    ep.coef_acc = 1.f;
+    ep.post = (it == 0) ? d.inv_norm[0] : 1.f;
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    gemm_tile<C, true>(B + r0 * mp, mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, lds);
+}
+
+// single-matrix variants for the test hooks
+template <class C, int PHASE>
+__global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
+                                                       int K, uint16_t* out, int64_t ld_out,
+                                                       float s2, float cb, float cc) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+    int ti, tj;
+    tri_index(blockIdx.x, ti, tj);
+    Epi ep;
+    ep.out = out;
+    ep.ld_out = ld_out;
+    ep.outT = (ti != tj) ? out : nullptr;
+    ep.ld_outT = ld_out;
+    if (PHASE == GRAM) {
+        ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = s2; ep.post = 1.f;
+    } else {
+        ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
+    }
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, lds);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __restrict__ X,
+                                                          const uint16_t* __restrict__ XT,
+                                                          const uint16_t* __restrict__ B,
+                                                          uint16_t* Xo, uint16_t* XoT, int m,
+                                                          int n, int64_t ldx, int64_t ldb, float ca,
+                                                          float s) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+    const int tcols = n / C::BN;
+    const int ti = blockIdx.x / tcols, tj = blockIdx.x - ti * tcols;
+    Epi ep;
+    ep.out = Xo; ep.ld_out = ldx; ep.outT = XoT; ep.ld_outT = ldb;
+    ep.E = X; ep.ld_e = ldx; ep.coef_e = ca; ep.coef_acc = 1.f; ep.post = s;
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    gemm_tile<C, true>(B + r0 * ldb, ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, lds);
+}
+
+using SymCfg = Cfg<256, 256, 2, 4>;
+using UpdCfg = Cfg<256, 256, 2, 4>;
+
+}  // namespace
+
+int gemm_tile_bf16() { return SymCfg::BM; }
+int upd_tile_m_bf16() { return UpdCfg::BM; }
+int upd_tile_n_bf16() { return UpdCfg::BN; }
+
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st) {
+    ns_sym_kernel<SymCfg, GRAM><<<total, SymCfg::NT, 0, st>>>(d, n, p.gram, it, 0.f, 0.f);
+    return hipGetLastError();
+}
+
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+                            hipStream_t st) {
+    ns_sym_kernel<SymCfg, POLY><<<total, SymCfg::NT, 0, st>>>(d, n, p.gram, 0, b, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
+                              hipStream_t st) {
+    ns_update_kernel<UpdCfg><<<total, UpdCfg::NT, 0, st>>>(d, n, p.upd, it, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
+                                   float s2, hipStream_t st) {
+    const int T = m / SymCfg::BM;
+    ns_sym_single<SymCfg, GRAM><<<T * (T + 1) / 2, SymCfg::NT, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(X), ldx, n, reinterpret_cast<uint16_t*>(A), lda, s2, 0.f,
+        0.f);
+    return hipGetLastError();
+}
+
+hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
+                                   hipStream_t st) {
+    const int T = m / SymCfg::BM;
+    ns_sym_single<SymCfg, POLY><<<T * (T + 1) / 2, SymCfg::NT, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, b,
+        c);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* B, void* Xo,
+                                     void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
+                                     float s, hipStream_t st) {
+    const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
+    ns_update_single<UpdCfg><<<tiles, UpdCfg::NT, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(XT),
+        reinterpret_cast<const uint16_t*>(B), reinterpret_cast<uint16_t*>(Xo),
+        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s);
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,139 @@
+// Internal declarations shared by the HIP sources of libmuon (gfx950 only).
+//
+// Device-side view of one Muon matrix, the workspace layout and the launch
+// wrappers of every kernel.  Nothing here is part of the public ABI
+// (include/muon.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/muon.h"
+
+namespace muon {
+
+// Canonical Newton-Schulz buffers are padded to these multiples so the GEMM
+// kernels run on whole tiles with no bounds checks.  The padding is zero and
+// the iteration keeps it zero: rows/cols of zeros stay zero under X X^T,
+// b A + c A A and a X + B X.
+constexpr int kPadBf16 = 256;
+constexpr int kPadF32 = 64;
+// Elementwise kernels (momentum, apply) work on 64 x 64 tiles of the weight.
+constexpr int kEwTile = 64;
+
+// One matrix as the kernels see it.  Built on the host, copied into the
+// workspace once per call.
+struct MatDesc {
+    // caller tensors
+    void* param;
+    const void* grad;
+    float* mom;
+    float* update_out;
+    float* norm_out;
+    int64_t rows, cols;
+    int64_t ld_param, ld_grad, ld_mom;
+    int32_t param_dtype, grad_dtype;
+    int32_t transposed;  // rows > cols: the iteration runs on W^T
+    int32_t mp, np;      // padded canonical dims: m' = min, n' = max
+    int32_t rows_pad, cols_pad;
+    int32_t ew_tiles_c;  // elementwise tiles along cols_pad
+    int32_t ew_tiles;    // elementwise tiles of this matrix
+    int32_t vec4;        // 1: every row start of param/grad/mom is 16B aligned and cols % 4 == 0
+    float scale;         // shape multiplier * extra_scale
+    // workspace buffers (bf16 or f32 elements by ns dtype)
+    void* x[2];   // canonical X, mp x np, ld np (ping-pong)
+    void* xt[2];  // X^T, np x mp, ld mp (ping-pong)
+    void* a;      // A = X X^T, mp x mp
+    void* b;      // B = b A + c A A, mp x mp
+    float* partials;  // one sum of squares per elementwise tile
+    float* inv_norm;  // s = 1/(||Y||_F + eps)
+};
+
+// Grouped launches: workgroup -> (matrix, local tile) through prefix sums of
+// tiles per matrix (int32 entries, n+1 of them).
+struct Prefix {
+    const int32_t* ew;
+    const int32_t* gram;  // triangle tiles (Gram and polynomial)
+    const int32_t* upd;   // full tiles of the update
+};
+
+__device__ __forceinline__ int find_matrix(const int32_t* prefix, int n, int32_t tile) {
+    // largest i with prefix[i] <= tile (prefix[0] = 0, prefix[n] = total)
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (__builtin_nontemporal_load(prefix + mid) <= tile) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---- bf16 helpers (round to nearest even, as a hardware conversion) -------
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---- launch wrappers ------------------------------------------------------
+// All return hipGetLastError() after the launch.
+hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
+                           int nesterov, int ns_f32, hipStream_t st);
+hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t st);
+hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
+                        float lr, float wd, int ns_f32, hipStream_t st);
+
+// bf16 Newton-Schulz phases over all matrices.  `it` is the iteration index
+// (0-based): it selects the ping-pong buffers and, for it == 0, folds the
+// normalisation s = 1/(||Y||+eps) into the epilogues.
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+                            hipStream_t st);
+hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
+                              hipStream_t st);
+int gemm_tile_bf16();  // square tile edge of the Gram/polynomial kernels
+int upd_tile_m_bf16();
+int upd_tile_n_bf16();
+
+hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
+hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+                           hipStream_t st);
+hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, float a,
+                             hipStream_t st);
+constexpr int kTileF32 = 64;
+
+// single-phase test hooks (one matrix, caller buffers)
+hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
+                                   float s2, hipStream_t st);
+hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
+                                   hipStream_t st);
+hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* B, void* Xo,
+                                     void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
+                                     float s, hipStream_t st);
+
+// AdamW: tensors travel in kernel arguments, kAdamwGroup per launch.
+constexpr int kAdamwGroup = 32;
+struct AdamwGroup {
+    void* param[kAdamwGroup];
+    const void* grad[kAdamwGroup];
+    float* m[kAdamwGroup];
+    float* v[kAdamwGroup];
+    int64_t numel[kAdamwGroup];
+    int32_t block_prefix[kAdamwGroup + 1];
+    uint8_t param_bf16[kAdamwGroup];
+    uint8_t grad_bf16[kAdamwGroup];
+    uint8_t vec4[kAdamwGroup];
+    int32_t count;
+};
+constexpr int kAdamwChunk = 4096;  // elements per workgroup
+hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,
+                        float eps, float wd, float bc1, float bc2, hipStream_t st);
+
+}  // namespace muon

@@ -1,0 +1,94 @@
+"""Shared test helpers: run workloads through libmuon and the oracle.
+
+The GPU side goes through the C ABI (the binding in muon_step_02_amd); the
+reference side is the fp64 oracle fed with the exact values the GPU saw.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+import muon_step_02_amd as mu
+
+# Tolerances (relative Frobenius error per matrix or tensor):
+TOL_O_BF16 = 3e-2   # Newton-Schulz output with bf16 operands
+TOL_O_F32 = 1e-4    # Newton-Schulz output in fp32
+TOL_STATE = 1e-6    # fp32 momentum and AdamW state
+
+
+def relF(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    num = np.linalg.norm(got - want)
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def w_tolerance(lr, s, O_ref, W_ref, tol_o):
+    """Bound on the weight's relative error implied by the update's: the
+    weight moves by lr*s*O, so an error tol_o*||O|| in O moves it by
+    lr*s*tol_o*||O||; plus fp32 rounding of W itself."""
+    return (lr * s * tol_o * np.linalg.norm(O_ref)) / max(np.linalg.norm(W_ref), 1e-30) + 2e-6
+
+
+class Handle:
+    _h = None
+
+    @classmethod
+    def get(cls):
+        if cls._h is None:
+            cls._h = mu.muon_init(0)
+        return cls._h
+
+
+def run_muon_step(mats, hp, stream=None, ws=None):
+    """One batched step on the current stream; returns the workspace used."""
+    h = Handle.get()
+    need = mu.muon_workspace_size(h, mats, hp)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    mu.muon_step_batched(h, mats, hp, ws, stream)
+    return ws
+
+
+def hp_from(muon_hp, **over):
+    d = dict(muon_hp)
+    d.update(over)
+    return mu.muon_hparams(lr=d["lr"], momentum=d["mu"], weight_decay=d["weight_decay"],
+                           eps=d["eps"], extra_scale=d.get("extra_scale", 1.0),
+                           nesterov=d["nesterov"], ns_steps=d["steps"], ns_dtype=d["ns_dtype"],
+                           scale_mode=d["scale_mode"], coeffs=d.get("coeffs"))
+
+
+def oracle_kwargs(muon_hp, **over):
+    d = dict(muon_hp)
+    d.update(over)
+    coeffs = d.get("coeffs")
+    if coeffs is not None:
+        coeffs = np.asarray(coeffs, dtype=np.float64).reshape(d["steps"], 3)
+    return dict(lr=d["lr"], mu=d["mu"], weight_decay=d["weight_decay"], nesterov=d["nesterov"],
+                eps=d["eps"], steps=d["steps"], coeffs=coeffs, scale_mode=d["scale_mode"],
+                extra_scale=d.get("extra_scale", 1.0))
+
+
+def compare_matrix(W0, G, M0, W1, M1, O_gpu, muon_hp, tol_o, report=None, name=""):
+    """Oracle step for one matrix from the exact inputs; assert parity."""
+    kw = oracle_kwargs(muon_hp)
+    Wr, Mr, Or = oracle.muon_matrix_step(W0, G, M0, **kw)
+    eo = relF(O_gpu, Or)
+    em = relF(M1, Mr)
+    s = oracle.shape_scale(W0.shape[0], W0.shape[1], kw["scale_mode"]) * kw["extra_scale"]
+    ew = relF(W1, Wr)
+    tw = w_tolerance(kw["lr"], s, Or, Wr, tol_o)
+    if report is not None:
+        report.append((name, W0.shape, eo, em, ew, tw))
+    assert eo <= tol_o, (name, "O", eo, tol_o)
+    assert em <= TOL_STATE, (name, "M", em)
+    assert ew <= tw, (name, "W", ew, tw)
+    return eo, em, ew
