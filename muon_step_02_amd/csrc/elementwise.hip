@@ -141,26 +141,35 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     const int64_t ld_nat = d.cols_pad, ld_trn = d.rows_pad;
     const float omm = 1.f - mu;
     float ss = 0.f;
+    // all loads of the thread's four rows first, so they are in flight together
+    Vals4 g[4], m[4];
+    int valid[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int64_t r = r0 + rr + 16 * q;
+        const int64_t cv = cols - (c0 + cg);
+        valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
+        if (valid[q] > 0) {
+            g[q] = load4<VEC>(d.grad, gbf, r * d.ld_grad + c0 + cg, valid[q]);
+            m[q] = load4<VEC>(d.mom, 0, r * d.ld_mom + c0 + cg, valid[q]);
+        }
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int lr = rr + 16 * q;
         const int64_t r = r0 + lr;
         const int64_t c = c0 + cg;
         float y[4] = {0.f, 0.f, 0.f, 0.f};
-        const int64_t cv = cols - c;
-        const int valid = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
-        if (valid > 0) {
-            Vals4 g = load4<VEC>(d.grad, gbf, r * d.ld_grad + c, valid);
-            Vals4 m = load4<VEC>(d.mom, 0, r * d.ld_mom + c, valid);
+        if (valid[q] > 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float mn = mu * m.v[e] + omm * g.v[e];
-                m.v[e] = mn;
-                const float yy = nesterov ? (omm * g.v[e] + mu * mn) : mn;
-                y[e] = (e < valid) ? yy : 0.f;
+                const float mn = mu * m[q].v[e] + omm * g[q].v[e];
+                m[q].v[e] = mn;
+                const float yy = nesterov ? (omm * g[q].v[e] + mu * mn) : mn;
+                y[e] = (e < valid[q]) ? yy : 0.f;
                 ss += y[e] * y[e];
             }
-            store4<VEC>(d.mom, 0, r * d.ld_mom + c, m, valid);
+            store4<VEC>(d.mom, 0, r * d.ld_mom + c, m[q], valid[q]);
         }
         store_ns4<NS_F32>(nat, r * ld_nat + c, y);
 #pragma unroll
@@ -229,24 +238,32 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
     const void* O = d.transposed ? d.xt[parity] : d.x[parity];
     const int64_t ld_o = d.cols_pad;
     const float sc = step * d.scale;
+    float o[4][4];
+    Vals4 w[4];
+    int valid[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int64_t r = r0 + rr + 16 * q;
-        const int64_t c = c0 + cg;
-        const int64_t cv = cols - c;
-        if (r >= rows || cv <= 0) continue;
-        const int valid = cv >= 4 ? 4 : (int)cv;
-        float o[4];
-        load_ns4<NS_F32>(O, r * ld_o + c, o);
-        Vals4 w = load4<VEC>(d.param, pbf, r * d.ld_param + c, valid);
+        const int64_t cv = cols - (c0 + cg);
+        valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
+        if (valid[q] > 0) {
+            load_ns4<NS_F32>(O, r * ld_o + c0 + cg, o[q]);
+            w[q] = load4<VEC>(d.param, pbf, r * d.ld_param + c0 + cg, valid[q]);
+        }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w.v[e] = decay * w.v[e] - sc * o[e];
-        store4<VEC>(d.param, pbf, r * d.ld_param + c, w, valid);
+    for (int q = 0; q < 4; ++q) {
+        if (valid[q] == 0) continue;
+        const int64_t r = r0 + rr + 16 * q;
+        const int64_t c = c0 + cg;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[q].v[e] = decay * w[q].v[e] - sc * o[q][e];
+        store4<VEC>(d.param, pbf, r * d.ld_param + c, w[q], valid[q]);
         if (d.update_out) {
             Vals4 ov;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ov.v[e] = o[e];
-            store4<false>(d.update_out, 0, r * cols + c, ov, valid);
+            for (int e = 0; e < 4; ++e) ov.v[e] = o[q][e];
+            store4<false>(d.update_out, 0, r * cols + c, ov, valid[q]);
         }
     }
 }

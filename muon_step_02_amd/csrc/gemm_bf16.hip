@@ -27,7 +27,8 @@
 // fp32 accumulation).  K advances in slabs of 64: operand slabs are copied
 // global->LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
 // staging) into two LDS stages, so the copy of slab k+1 overlaps the MFMAs
-// on slab k.  An LDS row is 64 bf16 = 8 chunks of 16 bytes; chunk c of row r
+// on slab k.  The epilogue goes through LDS so that every global access is a
+// coalesced 16-byte one.  An LDS row is 64 bf16 = 8 chunks of 16 bytes; chunk c of row r
 // lives at position c ^ (r & 7), so the 32 lanes of a fragment read (32
 // consecutive rows, one chunk) spread over all banks.
 //
@@ -53,9 +54,15 @@ struct Cfg {
     static constexpr int NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per stage
+    static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
+    static constexpr int LPS = ((BM + BN) / 8) / NW;  // slab copies per stage per wave
+    // epilogue: bands of RB rows staged as fp32 in one stage buffer
+    static constexpr int LDW = BN + 4;
+    static constexpr int RB = 32;
+    static_assert(RB * LDW * 4 <= STAGE * 2, "epilogue band must fit one stage");
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 MFMA tile");
     static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "slab rows must split over waves");
+    static_assert((RB * BN / 8) % NT == 0 && (BN * RB / 8) % NT == 0, "epilogue chunks must split");
 };
 
 // Copy rows [0, R) x k-chunk [0, 64) of a row-major bf16 operand (rows start
@@ -91,23 +98,49 @@ struct Epi {
     int64_t ld_out;
     uint16_t* outT;
     int64_t ld_outT;
-    // term added in the epilogue: coef_e * E[i][j] (E may be null)
+    // v = post * (coef_acc * product + coef_e * E[i][j])   (E only if HAS_E)
     const uint16_t* E;
     int64_t ld_e;
     float coef_e;
-    float coef_acc;  // multiplies the product
-    float post;      // multiplies the sum
+    float coef_acc;
+    float post;
 };
 
-// C tile (ti, tj) = sum_k P[i][k] Q[j][k]; P rows start at P0 (tile row 0),
-// Q rows at Q0.  K is a multiple of 64.
+template <class C>
+__device__ __forceinline__ void mfma_stage(const uint16_t* sp, f32x16 (&acc)[C::FM][C::FN], int wm,
+                                           int wn, int frow, int khalf) {
+    const uint16_t* sq = sp + C::BM * C::BK;
+#pragma unroll
+    for (int kk = 0; kk < C::BK / 16; ++kk) {
+        const int lch = 2 * kk + khalf;
+        bf16x8 a[C::FM], b[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) a[i] = read_frag(sp, wm * C::TM + i * 32 + frow, lch);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) b[j] = read_frag(sq, wn * C::TN + j * 32 + frow, lch);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// C tile = sum_k P[i][k] Q[j][k] for the BM rows starting at P0 and the BN
+// rows starting at Q0 (both leading dimension ld, K a multiple of 64), then
+// the epilogue.  s0 and s1 are the two LDS stages; they must be
+// distinct __shared__ variables so the compiler can tell that the copy into
+// one stage does not alias the fragment reads from the other (otherwise it
+// waits for every outstanding copy before each read and the prefetch is lost).
 template <class C, bool HAS_E>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64_t ldp,
-                                          const uint16_t* __restrict__ Q0, int64_t ldq, int K,
-                                          int64_t row0, int64_t col0, const Epi& ep, uint16_t* lds) {
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const uint16_t* __restrict__ Q0,
+                                          int64_t ld, int K, int64_t row0, int64_t col0,
+                                          const Epi& ep, uint16_t* s0, uint16_t* s1) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
 
     f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -118,81 +151,112 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int KT = K / C::BK;
-    // stage s: P slab at lds + s*STAGE, Q slab right after it
-    load_slab<C::BM, C::NW>(P0, ldp, lds, wave, lane);
-    load_slab<C::BN, C::NW>(Q0, ldq, lds + C::BM * C::BK, wave, lane);
-
-    const int frow = lane & 31;
-    const int khalf = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's slab copies landed
-        __syncthreads();                     // ... and every other wave's
-        const uint16_t* sp = lds + (kt & 1) * C::STAGE;
-        const uint16_t* sq = sp + C::BM * C::BK;
-        if (kt + 1 < KT) {
-            uint16_t* np_ = lds + ((kt + 1) & 1) * C::STAGE;
-            const int64_t k0 = (int64_t)(kt + 1) * C::BK;
-            load_slab<C::BM, C::NW>(P0 + k0, ldp, np_, wave, lane);
-            load_slab<C::BN, C::NW>(Q0 + k0, ldq, np_ + C::BM * C::BK, wave, lane);
-        }
+    load_slab<C::BM, C::NW>(P0, ld, s0, wave, lane);
+    load_slab<C::BN, C::NW>(Q0, ld, s0 + C::BM * C::BK, wave, lane);
+    for (int kt0 = 0; kt0 < KT; kt0 += 2) {
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 16; ++kk) {
-            const int lch = 2 * kk + khalf;
-            bf16x8 a[C::FM], b[C::FN];
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i) a[i] = read_frag(sp, wm * C::TM + i * 32 + frow, lch);
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) b[j] = read_frag(sq, wn * C::TN + j * 32 + frow, lch);
-#pragma unroll
-            for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-    }
-
-    // Epilogue.  MFMA 32x32 output layout: lane l, register r holds
-    // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31.  For each row of
-    // fragments the E terms are loaded first (one wait), then combined and
-    // stored.
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-        float e[C::FN][16];
-        if (HAS_E) {
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-                const int64_t col = col0 + wn * C::TN + j * 32 + frow;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t row = row0 + wm * C::TM + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                    e[j][r] = bf16_bits_to_f32(ep.E[row * ep.ld_e + col]);
+        for (int u = 0; u < 2; ++u) {
+            const int kt = kt0 + u;
+            if (kt < KT) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of stage u landed
+                __syncthreads();                     // ... and every other wave's
+                if (kt + 1 < KT) {
+                    uint16_t* dst = u == 0 ? s1 : s0;
+                    const int64_t k0 = (int64_t)(kt + 1) * C::BK;
+                    load_slab<C::BM, C::NW>(P0 + k0, ld, dst, wave, lane);
+                    load_slab<C::BN, C::NW>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
                 }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-            const int64_t col = col0 + wn * C::TN + j * 32 + frow;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t rb = row0 + wm * C::TM + i * 32 + 8 * q + 4 * khalf;
-                float v[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float x = ep.coef_acc * acc[i][j][4 * q + r];
-                    if (HAS_E) x += ep.coef_e * e[j][4 * q + r];
-                    v[r] = ep.post * x;
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) ep.out[(rb + r) * ep.ld_out + col] = f32_to_bf16_bits(v[r]);
-                if (ep.outT) {
-                    uint2 u;
-                    u.x = pack2(v[0], v[1]);
-                    u.y = pack2(v[2], v[3]);
-                    *reinterpret_cast<uint2*>(ep.outT + col * ep.ld_outT + rb) = u;
-                }
+                mfma_stage<C>(u == 0 ? s0 : s1, acc, wm, wn, frow, khalf);
             }
         }
     }
+
+    // Epilogue through LDS, in bands of RB rows: the waves holding the band
+    // write their fp32 accumulators (MFMA 32x32 layout: lane l, register r is
+    // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
+    // combines 8 consecutive columns with E and stores 16 bytes of the output,
+    // and, for the transposed copy, 8 consecutive rows of one column.
+    float* st = reinterpret_cast<float*>(s0);
+#pragma unroll 1
+    for (int band = 0; band < C::BM / C::RB; ++band) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            const int fr0 = wm * C::TM + i * 32;
+            if (fr0 >= band * C::RB && fr0 < (band + 1) * C::RB) {
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int c = wn * C::TN + j * 32 + frow;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = fr0 - band * C::RB + 8 * (r >> 2) + 4 * khalf + (r & 3);
+                        st[rr * C::LDW + c] = acc[i][j][r];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        const int64_t brow = row0 + (int64_t)band * C::RB;
+#pragma unroll
+        for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
+            const int ch = q * C::NT + threadIdx.x;
+            const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
+            const float4 a0 = *reinterpret_cast<const float4*>(st + rr * C::LDW + c8);
+            const float4 a1 = *reinterpret_cast<const float4*>(st + rr * C::LDW + c8 + 4);
+            float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            if (HAS_E) {
+                const uint4 ev = *reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8);
+                const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = ew[e >> 1];
+                    const float xe = __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+                    v[e] = ep.post * (ep.coef_acc * v[e] + ep.coef_e * xe);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = ep.post * (ep.coef_acc * v[e]);
+            }
+            uint4 o;
+            o.x = pack2(v[0], v[1]);
+            o.y = pack2(v[2], v[3]);
+            o.z = pack2(v[4], v[5]);
+            o.w = pack2(v[6], v[7]);
+            *reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8) = o;
+            if (ep.outT) {
+                *reinterpret_cast<float4*>(st + rr * C::LDW + c8) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(st + rr * C::LDW + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+        if (ep.outT) {
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
+                const int ch = q * C::NT + threadIdx.x;
+                const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = st[(i8 + e) * C::LDW + c];
+                uint4 o;
+                o.x = pack2(v[0], v[1]);
+                o.y = pack2(v[2], v[3]);
+                o.z = pack2(v[4], v[5]);
+                o.w = pack2(v[6], v[7]);
+                *reinterpret_cast<uint4*>(ep.outT + (col0 + c) * ep.ld_outT + brow + i8) = o;
+            }
+        }
+    }
+}
+
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumbering b -> (b % 8) * per + b / 8 gives each XCD a contiguous
+// range of tiles, so the tiles sharing operand slabs share one L2.  The grid
+// is 8 * per workgroups; numbers past `total` exit.
+__device__ __forceinline__ int xcd_tile(int total) {
+    const int per = (int)(gridDim.x >> 3);
+    const int b = (int)blockIdx.x;
+    const int t = (b & 7) * per + (b >> 3);
+    return t < total ? t : -1;
 }
 
 __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
@@ -203,13 +267,27 @@ __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
     tj = lt - t * (t + 1) / 2;
 }
 
+// Update tiles in groups of GRP tile-rows: within a group the column index
+// advances slowest, so concurrently running tiles reuse a few B row-slabs and
+// X^T row-slabs.
+constexpr int kUpdGroup = 8;
+__device__ __forceinline__ void grouped_index(int lt, int trows, int tcols, int& ti, int& tj) {
+    const int g = lt / (kUpdGroup * tcols);
+    const int rows_in = min(kUpdGroup, trows - g * kUpdGroup);
+    const int in = lt - g * kUpdGroup * tcols;
+    ti = g * kUpdGroup + in % rows_in;
+    tj = in / rows_in;
+}
+
 // Gram and polynomial: SYRK-like over the lower triangle of tiles.
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict__ descs, int n,
-                                                       const int32_t* __restrict__ prefix, int it,
-                                                       float cb, float cc) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
-    const int tile = blockIdx.x;
+                                                       const int32_t* __restrict__ prefix, int total,
+                                                       int it, float cb, float cc) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    const int tile = xcd_tile(total);
+    if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     int ti, tj;
@@ -241,21 +319,23 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, lds);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, s0, s1);
 }
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
                                                           const int32_t* __restrict__ prefix,
-                                                          int it, float ca) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
-    const int tile = blockIdx.x;
+                                                          int total, int it, float ca) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    const int tile = xcd_tile(total);
+    if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
     const int64_t mp = d.mp, np = d.np;
-    const int tcols = (int)(np / C::BN);
-    const int ti = lt / tcols, tj = lt - ti * tcols;
+    int ti, tj;
+    grouped_index(lt, (int)(mp / C::BM), (int)(np / C::BN), ti, tj);
     const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
     const uint16_t* XT = reinterpret_cast<const uint16_t*>(d.xt[it & 1]);
     Epi ep;
@@ -269,17 +349,20 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     ep.coef_acc = 1.f;
     ep.post = (it == 0) ? d.inv_norm[0] : 1.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * mp, mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, lds);
+    gemm_tile<C, true>(B + r0 * mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, s0, s1);
 }
 
 // single-matrix variants for the test hooks
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
                                                        int K, uint16_t* out, int64_t ld_out,
-                                                       float s2, float cb, float cc) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
+                                                       float s2, float cb, float cc, int total) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    const int tile = xcd_tile(total);
+    if (tile < 0) return;
     int ti, tj;
-    tri_index(blockIdx.x, ti, tj);
+    tri_index(tile, ti, tj);
     Epi ep;
     ep.out = out;
     ep.ld_out = ld_out;
@@ -291,7 +374,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
         ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, lds);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, K, r0, c0, ep, s0, s1);
 }
 
 template <class C>
@@ -300,16 +383,21 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* Xo, uint16_t* XoT, int m,
                                                           int n, int64_t ldx, int64_t ldb, float ca,
-                                                          float s) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[2 * C::STAGE];
-    const int tcols = n / C::BN;
-    const int ti = blockIdx.x / tcols, tj = blockIdx.x - ti * tcols;
+                                                          float s, int total) {
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    const int tile = xcd_tile(total);
+    if (tile < 0) return;
+    int ti, tj;
+    grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
     Epi ep;
     ep.out = Xo; ep.ld_out = ldx; ep.outT = XoT; ep.ld_outT = ldb;
     ep.E = X; ep.ld_e = ldx; ep.coef_e = ca; ep.coef_acc = 1.f; ep.post = s;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * ldb, ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, lds);
+    gemm_tile<C, true>(B + r0 * ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, s0, s1);
 }
+
+inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
 
 using SymCfg = Cfg<256, 256, 2, 4>;
 using UpdCfg = Cfg<256, 256, 2, 4>;
@@ -321,37 +409,39 @@ int upd_tile_m_bf16() { return UpdCfg::BM; }
 int upd_tile_n_bf16() { return UpdCfg::BN; }
 
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st) {
-    ns_sym_kernel<SymCfg, GRAM><<<total, SymCfg::NT, 0, st>>>(d, n, p.gram, it, 0.f, 0.f);
+    ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
     return hipGetLastError();
 }
 
 hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
                             hipStream_t st) {
-    ns_sym_kernel<SymCfg, POLY><<<total, SymCfg::NT, 0, st>>>(d, n, p.gram, 0, b, c);
+    ns_sym_kernel<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
     return hipGetLastError();
 }
 
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
                               hipStream_t st) {
-    ns_update_kernel<UpdCfg><<<total, UpdCfg::NT, 0, st>>>(d, n, p.upd, it, a);
+    ns_update_kernel<UpdCfg><<<xcd_grid(total), UpdCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
                                    float s2, hipStream_t st) {
     const int T = m / SymCfg::BM;
-    ns_sym_single<SymCfg, GRAM><<<T * (T + 1) / 2, SymCfg::NT, 0, st>>>(
+    const int total = T * (T + 1) / 2;
+    ns_sym_single<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), ldx, n, reinterpret_cast<uint16_t*>(A), lda, s2, 0.f,
-        0.f);
+        0.f, total);
     return hipGetLastError();
 }
 
 hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
                                    hipStream_t st) {
     const int T = m / SymCfg::BM;
-    ns_sym_single<SymCfg, POLY><<<T * (T + 1) / 2, SymCfg::NT, 0, st>>>(
+    const int total = T * (T + 1) / 2;
+    ns_sym_single<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, b,
-        c);
+        c, total);
     return hipGetLastError();
 }
 
@@ -359,10 +449,10 @@ hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* 
                                      void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
                                      float s, hipStream_t st) {
     const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
-    ns_update_single<UpdCfg><<<tiles, UpdCfg::NT, 0, st>>>(
+    ns_update_single<UpdCfg><<<xcd_grid(tiles), UpdCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(XT),
         reinterpret_cast<const uint16_t*>(B), reinterpret_cast<uint16_t*>(Xo),
-        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s);
+        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s, tiles);
     return hipGetLastError();
 }
 
