@@ -188,16 +188,23 @@ def main():
         gemm[ph] = {"avg_ms": round(avg, 4), "launches": cnt, "tflops": round(tf, 1),
                     "frac": round(tf / peak_mm, 4)}
     dom = max(("gram", "poly", "update"), key=lambda p: phases[p][0])
-    # memory-bound kernels: algorithmic bytes per element
+    # memory-bound kernels.  Algorithmic bytes per element: momentum reads G
+    # and M, writes M and the bf16 Newton-Schulz input (G 4|2 + 4 + 4 + 2);
+    # apply reads W and O and writes W (4 + 2 + 4).  The momentum kernel also
+    # writes the transposed copy of the input (+2 B), counted in "actual".
     g_bytes = 2 if wl.tensors[wl.muon[0].tensor].grad_dtype == torch.bfloat16 else 4
-    ew_bytes = {"momentum": (g_bytes + 4 + 4 + 2) * el, "apply": (4 + 2 + 4) * el}
+    ns_b = 4 if hpd["ns_dtype"] == "fp32" else 2
+    ew_bytes = {"momentum": ((g_bytes + 4 + 4 + ns_b) * el, (g_bytes + 4 + 4 + 2 * ns_b) * el),
+                "apply": ((4 + ns_b + 4) * el, (4 + ns_b + 4) * el)}
     hbm = {}
-    for ph, b in ew_bytes.items():
+    for ph, (b, b_act) in ew_bytes.items():
         ms, cnt = phases[ph]
         avg = ms / max(cnt, 1)
         gbs = b / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
+        gbs_act = b_act / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
         hbm[ph] = {"avg_ms": round(avg, 4), "gb_s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                   "bytes_per_launch": b}
+                   "bytes_per_launch": b, "actual_gb_s": round(gbs_act, 1),
+                   "actual_frac": round(gbs_act / PEAK_HBM_GBS, 4)}
     if ats:
         ad_el = sum(int(np.prod(wl.tensors[i].shape)) for i in wl.adamw)
         ms, cnt = phases["adamw"]

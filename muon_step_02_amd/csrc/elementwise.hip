@@ -31,18 +31,40 @@ struct Vals4 {
     float v[4];
 };
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// Streaming accesses: every element of the optimizer's tensors is touched
+// once per kernel, so loads and stores bypass cache retention.
+__device__ __forceinline__ float4 ld_nt(const float* p) {
+    const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_nt(float* p, float4 v) {
+    const f32x4v t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4v*>(p));
+}
+__device__ __forceinline__ uint2 ld_nt(const uint16_t* p) {
+    const u32x2v t = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ void st_nt(uint16_t* p, uint2 v) {
+    const u32x2v t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2v*>(p));
+}
+
 template <bool VEC>
 __device__ __forceinline__ Vals4 load4(const void* base, int dtype_bf16, int64_t off, int valid) {
     Vals4 r;
     if (VEC) {
         if (dtype_bf16) {
-            uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+            uint2 u = ld_nt(reinterpret_cast<const uint16_t*>(base) + off);
             r.v[0] = __builtin_bit_cast(float, u.x << 16);
             r.v[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
             r.v[2] = __builtin_bit_cast(float, u.y << 16);
             r.v[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
         } else {
-            float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+            float4 f = ld_nt(reinterpret_cast<const float*>(base) + off);
             r.v[0] = f.x; r.v[1] = f.y; r.v[2] = f.z; r.v[3] = f.w;
         }
     } else {
@@ -68,10 +90,9 @@ __device__ __forceinline__ void store4(void* base, int dtype_bf16, int64_t off, 
             uint2 u;
             u.x = (uint32_t)f32_to_bf16_bits(r.v[0]) | ((uint32_t)f32_to_bf16_bits(r.v[1]) << 16);
             u.y = (uint32_t)f32_to_bf16_bits(r.v[2]) | ((uint32_t)f32_to_bf16_bits(r.v[3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = u;
+            st_nt(reinterpret_cast<uint16_t*>(base) + off, u);
         } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) =
-                make_float4(r.v[0], r.v[1], r.v[2], r.v[3]);
+            st_nt(reinterpret_cast<float*>(base) + off, make_float4(r.v[0], r.v[1], r.v[2], r.v[3]));
         }
     } else {
 #pragma unroll
@@ -103,10 +124,10 @@ __device__ __forceinline__ void store_ns4(void* base, int64_t off, const float* 
 template <bool NS_F32>
 __device__ __forceinline__ void load_ns4(const void* base, int64_t off, float* v) {
     if (NS_F32) {
-        float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+        float4 f = ld_nt(reinterpret_cast<const float*>(base) + off);
         v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
     } else {
-        uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+        uint2 u = ld_nt(reinterpret_cast<const uint16_t*>(base) + off);
         v[0] = __builtin_bit_cast(float, u.x << 16);
         v[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
         v[2] = __builtin_bit_cast(float, u.y << 16);
@@ -321,15 +342,15 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
             const int64_t off = start + q * 1024 + threadIdx.x * 4;
             Vals4 th = load4<true>(P, pbf, off, 4);
             Vals4 g = load4<true>(G, gbf, off, 4);
-            float4 m = *reinterpret_cast<const float4*>(M + off);
-            float4 v = *reinterpret_cast<const float4*>(V + off);
+            float4 m = ld_nt(M + off);
+            float4 v = ld_nt(V + off);
             adamw_elem(th.v[0], g.v[0], m.x, v.x, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             adamw_elem(th.v[1], g.v[1], m.y, v.y, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             adamw_elem(th.v[2], g.v[2], m.z, v.z, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             adamw_elem(th.v[3], g.v[3], m.w, v.w, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             store4<true>(P, pbf, off, th, 4);
-            *reinterpret_cast<float4*>(M + off) = m;
-            *reinterpret_cast<float4*>(V + off) = v;
+            st_nt(M + off, m);
+            st_nt(V + off, v);
         }
     } else {
         for (int64_t i = start + threadIdx.x; i < end; i += 256) {
