@@ -89,7 +89,16 @@ typedef struct muon_context* muon_handle;
  *              the first step).
  *   update_out optional (NULL = skip): dense rows x cols F32 array that
  *              receives O, the orthogonalised update before the multiplier.
- *   norm_out   optional (NULL = skip): one F32 that receives ||Y||_F. */
+ *   norm_out   optional (NULL = skip): one F32 that receives ||Y||_F.
+ *   qk_smax    optional (NULL = no clip): device F32 array, one maximum
+ *              attention logit S_max per block of qk_block_rows rows of W
+ *              (a query or key projection, one block per head).  After the
+ *              update every row of block h is multiplied by sqrt(gamma_h),
+ *              gamma_h = tau / S_max^h if S_max^h > tau, else 1, with tau =
+ *              muon_hparams.qk_tau ("The Optimizer Wars ...", section "What
+ *              is MuonClip?": QK-Clip rescales W_q^h and W_k^h by sqrt of
+ *              min(1, tau / S_max^h) after the Muon update).
+ *   qk_block_rows  rows per head block (>= 1 when qk_smax is set). */
 typedef struct {
     void* param;
     const void* grad;
@@ -100,6 +109,8 @@ typedef struct {
     int64_t ld_param, ld_grad, ld_mom;
     int32_t param_dtype; /* muon_dtype */
     int32_t grad_dtype;  /* muon_dtype */
+    const float* qk_smax;
+    int64_t qk_block_rows;
 } muon_matrix;
 
 /* Step hyperparameters, shared by every matrix of one call.
@@ -118,6 +129,7 @@ typedef struct {
     int32_t ns_dtype;   /* muon_dtype */
     int32_t scale_mode; /* muon_scale_mode */
     const float* coeffs;
+    float qk_tau;       /* QK-Clip threshold (100 in Kimi K2); used only by matrices with qk_smax */
 } muon_hparams;
 
 /* One AdamW tensor (flat, numel elements, contiguous).  param F32 or BF16;
@@ -168,7 +180,8 @@ muon_status muon_workspace_size(muon_handle h, const muon_matrix* mats, int n,
  * descriptor array is host memory, read during the call only.  Rejects:
  * n < 1, rows or cols < 1, ld < cols, a null param/grad/momentum, an unknown
  * dtype or mode, ns_steps < 1, lr/momentum non-finite, overlapping
- * param/grad/momentum ranges within a matrix, a small or null workspace. */
+ * param/grad/momentum ranges within a matrix, a small or null workspace,
+ * qk_block_rows outside [1, rows] when qk_smax is set, qk_tau < 0. */
 muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                               const muon_hparams* hp, void* workspace,
                               size_t workspace_bytes, void* stream);
@@ -196,6 +209,22 @@ typedef struct {
 
 muon_status muon_profile_enable(muon_handle h, int enable);
 muon_status muon_profile_collect(muon_handle h, muon_phase_times* out);
+
+/* AdamW with the gradients first clipped together to a global Euclidean
+ * norm ("Por qué AdamW ...", section "Por qué AdamW, y por qué con esos
+ * números": before g enters m and v, if its norm exceeds 1 it is rescaled
+ * to 1).  norm = ||(g_1, ..., g_n)||_2 over all numel elements of all n
+ * tensors; every gradient is multiplied by max_norm / norm when norm >
+ * max_norm (the gradient tensors themselves are not modified).  norm_out
+ * (optional device float) receives the norm before clipping.  The reduction
+ * has a fixed order, so results are bitwise repeatable.  workspace: caller
+ * device memory of at least adamw_workspace_size bytes, 256-byte aligned.
+ * Rejects what adamw_step rejects, max_norm <= 0 or non-finite, and a small
+ * or null workspace. */
+muon_status adamw_workspace_size(muon_handle h, const adamw_tensor* ts, int n, size_t* bytes);
+muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
+                               const adamw_hparams* hp, float max_norm, float* norm_out,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human readable name of a status. */
 const char* muon_status_str(muon_status s);

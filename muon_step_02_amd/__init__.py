@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     MuonMatrix,
     adamw_hparams,
     adamw_step,
+    adamw_step_clipped,
+    adamw_workspace_size,
     adamw_tensor,
     exported_symbols,
     load,

@@ -32,6 +32,8 @@ SYMBOLS = (
     "muon_test_update_bf16",
     "muon_profile_enable",
     "muon_profile_collect",
+    "adamw_workspace_size",
+    "adamw_step_clipped",
 )
 
 NUM_PHASES = 7
@@ -58,6 +60,8 @@ class MuonMatrix(ctypes.Structure):
         ("ld_mom", ctypes.c_int64),
         ("param_dtype", ctypes.c_int32),
         ("grad_dtype", ctypes.c_int32),
+        ("qk_smax", ctypes.c_void_p),
+        ("qk_block_rows", ctypes.c_int64),
     ]
 
 
@@ -73,6 +77,7 @@ class MuonHparams(ctypes.Structure):
         ("ns_dtype", ctypes.c_int32),
         ("scale_mode", ctypes.c_int32),
         ("coeffs", ctypes.POINTER(ctypes.c_float)),
+        ("qk_tau", ctypes.c_float),
     ]
 
 
@@ -128,11 +133,16 @@ def load():
     lib.muon_test_gram_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, vp]
     lib.muon_test_poly_bf16.argtypes = [vp, vp, vp, i64, i64, f32, f32, vp]
     lib.muon_test_update_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
+    lib.adamw_workspace_size.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.adamw_step_clipped.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
+                                       ctypes.POINTER(AdamwHparams), f32, vp, vp, ctypes.c_size_t, vp]
     lib.muon_profile_enable.argtypes = [vp, i32]
     lib.muon_profile_collect.argtypes = [vp, ctypes.POINTER(PhaseTimes)]
     for name in ("muon_init", "muon_destroy", "muon_workspace_size", "muon_step_batched",
                  "adamw_step", "muon_test_gram_bf16", "muon_test_poly_bf16",
-                 "muon_test_update_bf16", "muon_profile_enable", "muon_profile_collect"):
+                 "muon_test_update_bf16", "muon_profile_enable", "muon_profile_collect",
+                 "adamw_workspace_size", "adamw_step_clipped"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -180,8 +190,11 @@ def _ld(t):
     return t.stride(0)
 
 
-def muon_matrix(param, grad, momentum, update_out=None, norm_out=None):
-    """Descriptor of one Muon matrix from 2D tensors (row blocks are fine)."""
+def muon_matrix(param, grad, momentum, update_out=None, norm_out=None, qk_smax=None,
+                qk_block_rows=0):
+    """Descriptor of one Muon matrix from 2D tensors (row blocks are fine).
+    ``qk_smax``: optional float32 device tensor of per-head max logits for
+    QK-Clip, one per ``qk_block_rows`` rows."""
     import torch
     if momentum.dtype != torch.float32:
         raise TypeError("momentum must be float32")
@@ -194,21 +207,28 @@ def muon_matrix(param, grad, momentum, update_out=None, norm_out=None):
             raise ValueError("update_out must be a contiguous float32 (rows, cols) tensor")
     if norm_out is not None and norm_out.dtype != torch.float32:
         raise ValueError("norm_out must be float32")
+    if qk_smax is not None:
+        if qk_smax.dtype != torch.float32 or not qk_smax.is_contiguous():
+            raise ValueError("qk_smax must be a contiguous float32 tensor")
+        if qk_block_rows < 1 or qk_smax.numel() * qk_block_rows < rows:
+            raise ValueError("qk_smax needs one value per qk_block_rows rows")
     return MuonMatrix(
         param=param.data_ptr(), grad=grad.data_ptr(), momentum=momentum.data_ptr(),
         update_out=update_out.data_ptr() if update_out is not None else None,
         norm_out=norm_out.data_ptr() if norm_out is not None else None,
         rows=rows, cols=cols, ld_param=_ld(param), ld_grad=_ld(grad), ld_mom=_ld(momentum),
-        param_dtype=_dt(param), grad_dtype=_dt(grad))
+        param_dtype=_dt(param), grad_dtype=_dt(grad),
+        qk_smax=qk_smax.data_ptr() if qk_smax is not None else None,
+        qk_block_rows=qk_block_rows if qk_smax is not None else 0)
 
 
 def muon_hparams(lr, momentum=0.95, weight_decay=0.1, eps=1e-7, extra_scale=1.0, nesterov=True,
-                 ns_steps=5, ns_dtype="bf16", scale_mode="moonlight", coeffs=None):
+                 ns_steps=5, ns_dtype="bf16", scale_mode="moonlight", coeffs=None, qk_tau=100.0):
     """Hyperparameters; ``coeffs`` is None or a flat list of 3*ns_steps floats."""
     hp = MuonHparams(lr=lr, momentum=momentum, weight_decay=weight_decay, eps=eps,
                      extra_scale=extra_scale, nesterov=1 if nesterov else 0, ns_steps=ns_steps,
                      ns_dtype=MUON_BF16 if ns_dtype == "bf16" else MUON_F32,
-                     scale_mode=SCALE_MODES[scale_mode])
+                     scale_mode=SCALE_MODES[scale_mode], qk_tau=qk_tau)
     if coeffs is not None:
         arr = (ctypes.c_float * len(coeffs))(*[float(c) for c in coeffs])
         hp._coeff_keepalive = arr
@@ -274,6 +294,26 @@ def adamw_step(h, tensors, hp, stream=None):
     arr = (AdamwTensor * len(tensors))(*tensors)
     _check(load().adamw_step(h, arr, len(tensors), ctypes.byref(hp), _stream_ptr(stream)),
            "adamw_step")
+
+
+def adamw_workspace_size(h, tensors):
+    arr = (AdamwTensor * len(tensors))(*tensors)
+    sz = ctypes.c_size_t()
+    _check(load().adamw_workspace_size(h, arr, len(tensors), ctypes.byref(sz)), "adamw_workspace_size")
+    return sz.value
+
+
+def adamw_step_clipped(h, tensors, hp, max_norm, workspace, norm_out=None, stream=None):
+    """AdamW with the gradients clipped together to global norm ``max_norm``.
+    ``workspace``: uint8 CUDA tensor of at least adamw_workspace_size bytes;
+    ``norm_out``: optional float32 CUDA tensor receiving the norm."""
+    arr = (AdamwTensor * len(tensors))(*tensors)
+    _check(load().adamw_step_clipped(h, arr, len(tensors), ctypes.byref(hp), float(max_norm),
+                                     ctypes.c_void_p(norm_out.data_ptr() if norm_out is not None else 0),
+                                     ctypes.c_void_p(workspace.data_ptr()),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(stream)),
+           "adamw_step_clipped")
 
 
 def muon_test_gram_bf16(h, X, A, m, n, ldx, lda, s2=1.0, stream=None):

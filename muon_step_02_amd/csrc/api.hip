@@ -102,6 +102,7 @@ muon_status check_hparams(const muon_hparams* hp) {
         !finite(hp->eps) || !finite(hp->extra_scale))
         return MUON_ERR_INVALID_ARG;
     if (hp->eps < 0.f) return MUON_ERR_INVALID_ARG;
+    if (!finite(hp->qk_tau) || hp->qk_tau < 0.f) return MUON_ERR_INVALID_ARG;
     if (hp->coeffs) {
         for (int i = 0; i < 3 * hp->ns_steps; ++i)
             if (!finite(hp->coeffs[i])) return MUON_ERR_INVALID_ARG;
@@ -117,6 +118,8 @@ muon_status check_matrix(const muon_matrix& m, bool need_ptrs) {
     if (!valid_dtype(m.param_dtype) || !valid_dtype(m.grad_dtype)) return MUON_ERR_INVALID_ARG;
     if (!need_ptrs) return MUON_OK;
     if (!m.param || !m.grad || !m.momentum) return MUON_ERR_INVALID_ARG;
+    if (m.qk_smax && (m.qk_block_rows < 1 || m.qk_block_rows > m.rows)) return MUON_ERR_INVALID_ARG;
+    if (m.qk_smax && reinterpret_cast<uintptr_t>(m.qk_smax) % 4) return MUON_ERR_UNALIGNED;
     const size_t pes = elem_bytes(m.param_dtype), ges = elem_bytes(m.grad_dtype);
     if (reinterpret_cast<uintptr_t>(m.param) % pes || reinterpret_cast<uintptr_t>(m.grad) % ges ||
         reinterpret_cast<uintptr_t>(m.momentum) % 4 ||
@@ -139,13 +142,26 @@ bool aligned_rows(const void* p, int64_t ld, size_t es) {
     return reinterpret_cast<uintptr_t>(p) % vec_bytes == 0 && ld % 4 == 0;
 }
 
-// Workspace plan for one call.
+// Workspace plan for one call.  Matrices are split into two classes with
+// their own GEMM tile size: "large" (256-wide tiles and padding) and, for
+// bf16 Newton-Schulz, "small" (short side <= 128: 128-wide tiles and
+// padding).  The descriptor table holds the large class first; each class has
+// its own prefix arrays of Gram/polynomial and update tiles, while the
+// elementwise kernels run over all matrices at once.
+struct ClassPlan {
+    int first = 0, count = 0;           // descriptor range
+    std::vector<int32_t> pgram, pupd;   // count + 1 entries each
+    size_t off_pgram = 0, off_pupd = 0;
+    int total_gram = 0, total_upd = 0;
+};
+
 struct Plan {
     std::vector<MatDesc> d;
-    std::vector<int32_t> pew, pgram, pupd;
-    size_t off_pew = 0, off_pgram = 0, off_pupd = 0, table_bytes = 0;
+    std::vector<int32_t> pew;
+    ClassPlan cls[2];  // 0 large, 1 small
+    size_t off_pew = 0, table_bytes = 0;
     size_t off_partials = 0, off_invnorm = 0, total = 0;
-    int total_ew = 0, total_gram = 0, total_upd = 0;
+    int total_ew = 0;
     int ns_f32 = 0;
 };
 
@@ -159,13 +175,12 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         if (st != MUON_OK) return st;
     }
     P.ns_f32 = hp->ns_dtype == MUON_F32;
-    const int64_t pad = P.ns_f32 ? kPadF32 : kPadBf16;
     const size_t es = P.ns_f32 ? 4 : 2;
-    const int symT = P.ns_f32 ? kTileF32 : gemm_tile_bf16();
-    const int updM = P.ns_f32 ? kTileF32 : upd_tile_m_bf16();
-    const int updN = P.ns_f32 ? kTileF32 : upd_tile_n_bf16();
+    auto is_small = [&](int i) {
+        return !P.ns_f32 && std::min(mats[i].rows, mats[i].cols) <= kSmallBf16;
+    };
 
-    // order by descending Newton-Schulz work
+    // order: large class first, each class by descending Newton-Schulz work
     std::vector<int> order(n);
     std::iota(order.begin(), order.end(), 0);
     auto work = [&](int i) {
@@ -173,21 +188,40 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         const double nn = (double)std::max(mats[i].rows, mats[i].cols);
         return m * m * nn;
     };
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        if (is_small(a) != is_small(b)) return !is_small(a);
+        return work(a) > work(b);
+    });
 
     P.d.assign(n, MatDesc{});
     P.pew.assign(n + 1, 0);
-    P.pgram.assign(n + 1, 0);
-    P.pupd.assign(n + 1, 0);
-    int64_t tew = 0, tgram = 0, tupd = 0;
+    int64_t tew = 0;
+    int nsmall = 0;
+    for (int i = 0; i < n; ++i) nsmall += is_small(i) ? 1 : 0;
+    P.cls[0].first = 0;
+    P.cls[0].count = n - nsmall;
+    P.cls[1].first = n - nsmall;
+    P.cls[1].count = nsmall;
+    for (int c = 0; c < 2; ++c) {
+        P.cls[c].pgram.assign(P.cls[c].count + 1, 0);
+        P.cls[c].pupd.assign(P.cls[c].count + 1, 0);
+    }
+    int64_t tgram[2] = {0, 0}, tupd[2] = {0, 0};
     for (int k = 0; k < n; ++k) {
         const muon_matrix& m = mats[order[k]];
+        const int c = k < P.cls[1].first ? 0 : 1;
+        const int64_t pad = P.ns_f32 ? kPadF32 : (c ? kSmallBf16 : kPadBf16);
+        const int symT = P.ns_f32 ? kTileF32 : gemm_tile_bf16(c);
+        const int updM = P.ns_f32 ? kTileF32 : upd_tile_m_bf16(c);
+        const int updN = P.ns_f32 ? kTileF32 : upd_tile_n_bf16(c);
         MatDesc& d = P.d[k];
         d.param = m.param;
         d.grad = m.grad;
         d.mom = m.momentum;
         d.update_out = m.update_out;
         d.norm_out = m.norm_out;
+        d.qk_smax = m.qk_smax;
+        d.qk_block_rows = m.qk_smax ? m.qk_block_rows : 0;
         d.rows = m.rows;
         d.cols = m.cols;
         d.ld_param = m.ld_param;
@@ -198,15 +232,8 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         d.transposed = m.rows > m.cols ? 1 : 0;
         d.rows_pad = (int32_t)pad_to(m.rows, pad);
         d.cols_pad = (int32_t)pad_to(m.cols, pad);
-        d.mp = std::min(d.rows_pad, d.cols_pad);
-        d.np = std::max(d.rows_pad, d.cols_pad);
-        if (d.transposed) {
-            d.mp = d.cols_pad;
-            d.np = d.rows_pad;
-        } else {
-            d.mp = d.rows_pad;
-            d.np = d.cols_pad;
-        }
+        d.mp = d.transposed ? d.cols_pad : d.rows_pad;
+        d.np = d.transposed ? d.rows_pad : d.cols_pad;
         d.ew_tiles_c = d.cols_pad / kEwTile;
         d.ew_tiles = (d.rows_pad / kEwTile) * d.ew_tiles_c;
         d.vec4 = need_ptrs && m.cols % 4 == 0 &&
@@ -218,24 +245,30 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         const int64_t gram_tiles = P.ns_f32 ? Ts * Ts : Ts * (Ts + 1) / 2;
         const int64_t upd_tiles = (d.mp / updM) * (d.np / updN);
         tew += d.ew_tiles;
-        tgram += gram_tiles;
-        tupd += upd_tiles;
-        if (tew > INT32_MAX || tgram > INT32_MAX || tupd > INT32_MAX) return MUON_ERR_INVALID_ARG;
+        tgram[c] += gram_tiles;
+        tupd[c] += upd_tiles;
+        if (tew > INT32_MAX || tgram[c] > INT32_MAX / 2 || tupd[c] > INT32_MAX / 2)
+            return MUON_ERR_INVALID_ARG;
         P.pew[k + 1] = (int32_t)tew;
-        P.pgram[k + 1] = (int32_t)tgram;
-        P.pupd[k + 1] = (int32_t)tupd;
+        const int kc = k - P.cls[c].first;
+        P.cls[c].pgram[kc + 1] = (int32_t)tgram[c];
+        P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
     }
     P.total_ew = (int)tew;
-    P.total_gram = (int)tgram;
-    P.total_upd = (int)tupd;
+    for (int c = 0; c < 2; ++c) {
+        P.cls[c].total_gram = (int)tgram[c];
+        P.cls[c].total_upd = (int)tupd[c];
+    }
 
     size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
     P.off_pew = off;
     off = align_up(off + (size_t)(n + 1) * 4, 256);
-    P.off_pgram = off;
-    off = align_up(off + (size_t)(n + 1) * 4, 256);
-    P.off_pupd = off;
-    off = align_up(off + (size_t)(n + 1) * 4, 256);
+    for (int c = 0; c < 2; ++c) {
+        P.cls[c].off_pgram = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+        P.cls[c].off_pupd = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+    }
     P.table_bytes = off;
     P.off_partials = off;
     off = align_up(off + (size_t)tew * 4, 256);
@@ -389,18 +422,25 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     memset(hb, 0, P.table_bytes);
     memcpy(hb, P.d.data(), (size_t)n * sizeof(MatDesc));
     memcpy(hb + P.off_pew, P.pew.data(), (size_t)(n + 1) * 4);
-    memcpy(hb + P.off_pgram, P.pgram.data(), (size_t)(n + 1) * 4);
-    memcpy(hb + P.off_pupd, P.pupd.data(), (size_t)(n + 1) * 4);
+    for (const ClassPlan& c : P.cls) {
+        memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
+        memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
+    }
     if (hipMemcpyAsync(workspace, hb, P.table_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
         return MUON_ERR_HIP;
     if (hipEventRecord(slot.ev, s) != hipSuccess) return MUON_ERR_HIP;
     slot.pending = true;
 
     const MatDesc* dd = reinterpret_cast<const MatDesc*>(workspace);
-    Prefix pf;
+    Prefix pf;  // elementwise kernels: all matrices
     pf.ew = reinterpret_cast<const int32_t*>(ws + P.off_pew);
-    pf.gram = reinterpret_cast<const int32_t*>(ws + P.off_pgram);
-    pf.upd = reinterpret_cast<const int32_t*>(ws + P.off_pupd);
+    pf.gram = pf.upd = nullptr;
+    Prefix pc[2];
+    for (int c = 0; c < 2; ++c) {
+        pc[c].ew = nullptr;
+        pc[c].gram = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pgram);
+        pc[c].upd = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pupd);
+    }
 
     hipError_t e = timed(h, 0, s, [&] {
         return launch_momentum(dd, n, pf, P.total_ew, hp->momentum, hp->nesterov, P.ns_f32, s);
@@ -414,30 +454,48 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             c = hp->coeffs[3 * it + 2];
         }
         if (P.ns_f32) {
-            e = timed(h, 2, s, [&] { return launch_gram_f32(dd, n, pf, P.total_gram, it, s); });
+            const ClassPlan& L = P.cls[0];
+            e = timed(h, 2, s, [&] { return launch_gram_f32(dd, L.count, pc[0], L.total_gram, it, s); });
             if (e == hipSuccess)
-                e = timed(h, 3, s, [&] { return launch_poly_f32(dd, n, pf, P.total_gram, b, c, s); });
+                e = timed(h, 3, s, [&] { return launch_poly_f32(dd, L.count, pc[0], L.total_gram, b, c, s); });
             if (e == hipSuccess)
-                e = timed(h, 4, s, [&] { return launch_update_f32(dd, n, pf, P.total_upd, it, a, s); });
-        } else {
-            e = timed(h, 2, s, [&] { return launch_gram_bf16(dd, n, pf, P.total_gram, it, s); });
-            if (e == hipSuccess)
-                e = timed(h, 3, s, [&] { return launch_poly_bf16(dd, n, pf, P.total_gram, b, c, s); });
-            if (e == hipSuccess)
-                e = timed(h, 4, s, [&] { return launch_update_bf16(dd, n, pf, P.total_upd, it, a, s); });
+                e = timed(h, 4, s, [&] { return launch_update_f32(dd, L.count, pc[0], L.total_upd, it, a, s); });
+            continue;
+        }
+        // the two classes' launches of one phase are independent of each other
+        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+            const ClassPlan& C = P.cls[k];
+            if (C.count == 0) continue;
+            const MatDesc* dc = dd + C.first;
+            e = timed(h, 2, s, [&] { return launch_gram_bf16(dc, C.count, pc[k], C.total_gram, it, k, s); });
+        }
+        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+            const ClassPlan& C = P.cls[k];
+            if (C.count == 0) continue;
+            const MatDesc* dc = dd + C.first;
+            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.total_gram, b, c, k, s); });
+        }
+        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+            const ClassPlan& C = P.cls[k];
+            if (C.count == 0) continue;
+            const MatDesc* dc = dd + C.first;
+            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.total_upd, it, a, k, s); });
         }
     }
     if (e == hipSuccess)
         e = timed(h, 5, s, [&] {
             return launch_apply(dd, n, pf, P.total_ew, hp->ns_steps & 1, hp->lr, hp->weight_decay,
-                                P.ns_f32, s);
+                                hp->qk_tau, P.ns_f32, s);
         });
     return hip_status(e);
 }
 
-muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n, const adamw_hparams* hp,
-                       void* stream) {
-    if (!h || !ts || n < 1 || !hp) return MUON_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+muon_status check_adamw(const adamw_tensor* ts, int n, const adamw_hparams* hp) {
+    if (!ts || n < 1 || !hp) return MUON_ERR_INVALID_ARG;
     if (hp->step < 1) return MUON_ERR_INVALID_ARG;
     if (!finite(hp->lr) || !finite(hp->beta1) || !finite(hp->beta2) || !finite(hp->eps) ||
         !finite(hp->weight_decay))
@@ -454,22 +512,23 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n, const adamw
             reinterpret_cast<uintptr_t>(t.grad) % elem_bytes(t.grad_dtype) ||
             reinterpret_cast<uintptr_t>(t.exp_avg) % 4 || reinterpret_cast<uintptr_t>(t.exp_avg_sq) % 4)
             return MUON_ERR_UNALIGNED;
-        if ((t.numel + kAdamwChunk - 1) / kAdamwChunk > INT32_MAX / 2) return MUON_ERR_INVALID_ARG;
+        if ((t.numel + kAdamwChunk - 1) / kAdamwChunk > INT32_MAX / 4) return MUON_ERR_INVALID_ARG;
     }
-    const double bc1 = 1.0 - pow((double)hp->beta1, (double)hp->step);
-    const double bc2 = 1.0 - pow((double)hp->beta2, (double)hp->step);
-    DeviceGuard g(h->device);
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return MUON_OK;
+}
+
+// Split the tensor list into launch groups (at most kAdamwGroup tensors and
+// INT32_MAX/4 blocks each) and call fn(group, blocks, first_block) per group.
+template <class F>
+hipError_t for_each_adamw_group(const adamw_tensor* ts, int n, F&& fn) {
     AdamwGroup grp;
     memset(&grp, 0, sizeof(grp));
-    int64_t blocks = 0;
+    int64_t blocks = 0, first = 0;
     auto flush = [&]() -> hipError_t {
         if (grp.count == 0) return hipSuccess;
         grp.block_prefix[grp.count] = (int32_t)blocks;
-        hipError_t e = timed(h, 6, s, [&] {
-            return launch_adamw(grp, (int)blocks, hp->lr, hp->beta1, hp->beta2, hp->eps,
-                                hp->weight_decay, (float)bc1, (float)bc2, s);
-        });
+        hipError_t e = fn(grp, (int)blocks, (int)first);
+        first += blocks;
         memset(&grp, 0, sizeof(grp));
         blocks = 0;
         return e;
@@ -478,9 +537,9 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n, const adamw
         const adamw_tensor& t = ts[i];
         if (t.numel == 0) continue;
         const int64_t nb = (t.numel + kAdamwChunk - 1) / kAdamwChunk;
-        if (grp.count == kAdamwGroup || blocks + nb > INT32_MAX / 2) {
+        if (grp.count == kAdamwGroup || blocks + nb > INT32_MAX / 4) {
             hipError_t e = flush();
-            if (e != hipSuccess) return MUON_ERR_HIP;
+            if (e != hipSuccess) return e;
         }
         const int k = grp.count++;
         grp.param[k] = t.param;
@@ -498,7 +557,78 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n, const adamw
                       reinterpret_cast<uintptr_t>(t.exp_avg_sq) % 16 == 0;
         blocks += nb;
     }
-    return hip_status(flush());
+    return flush();
+}
+
+int64_t adamw_total_blocks(const adamw_tensor* ts, int n) {
+    int64_t b = 0;
+    for (int i = 0; i < n; ++i)
+        if (ts[i].numel > 0) b += (ts[i].numel + kAdamwChunk - 1) / kAdamwChunk;
+    return b;
+}
+
+hipError_t adamw_launch_all(muon_context* h, const adamw_tensor* ts, int n, const adamw_hparams* hp,
+                            const float* gscale, hipStream_t s) {
+    const double bc1 = 1.0 - pow((double)hp->beta1, (double)hp->step);
+    const double bc2 = 1.0 - pow((double)hp->beta2, (double)hp->step);
+    return for_each_adamw_group(ts, n, [&](const AdamwGroup& grp, int blocks, int) {
+        return timed(h, 6, s, [&] {
+            return launch_adamw(grp, blocks, hp->lr, hp->beta1, hp->beta2, hp->eps,
+                                hp->weight_decay, (float)bc1, (float)bc2, gscale, s);
+        });
+    });
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n, const adamw_hparams* hp,
+                       void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    muon_status st = check_adamw(ts, n, hp);
+    if (st != MUON_OK) return st;
+    DeviceGuard g(h->device);
+    return hip_status(adamw_launch_all(h, ts, n, hp, nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+muon_status adamw_workspace_size(muon_handle h, const adamw_tensor* ts, int n, size_t* bytes) {
+    if (!h || !bytes || !ts || n < 1) return MUON_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i)
+        if (ts[i].numel < 0) return MUON_ERR_INVALID_ARG;
+    *bytes = align_up((size_t)adamw_total_blocks(ts, n) * 4, 256) + 256;
+    return MUON_OK;
+}
+
+muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
+                               const adamw_hparams* hp, float max_norm, float* norm_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    muon_status st = check_adamw(ts, n, hp);
+    if (st != MUON_OK) return st;
+    if (!finite(max_norm) || max_norm <= 0.f) return MUON_ERR_INVALID_ARG;
+    if (norm_out && reinterpret_cast<uintptr_t>(norm_out) % 4) return MUON_ERR_UNALIGNED;
+    const int64_t nblocks = adamw_total_blocks(ts, n);
+    const size_t need = align_up((size_t)nblocks * 4, 256) + 256;
+    const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
+    if (!workspace || ws % 256 || workspace_bytes < need) return MUON_ERR_WORKSPACE;
+    if (nblocks > INT32_MAX) return MUON_ERR_INVALID_ARG;
+    DeviceGuard g(h->device);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float* partials = reinterpret_cast<float*>(workspace);
+    float* scale = reinterpret_cast<float*>(ws + align_up((size_t)nblocks * 4, 256));
+    hipError_t e = hipSuccess;
+    if (nblocks > 0) {
+        e = for_each_adamw_group(ts, n, [&](const AdamwGroup& grp, int blocks, int first) {
+            return timed(h, 6, s, [&] { return launch_adamw_sumsq(grp, blocks, partials, first, s); });
+        });
+    }
+    if (e == hipSuccess)
+        e = timed(h, 6, s, [&] {
+            return launch_clip_finalize(partials, (int)nblocks, max_norm, scale, norm_out, s);
+        });
+    if (e == hipSuccess) e = adamw_launch_all(h, ts, n, hp, scale, s);
+    return hip_status(e);
 }
 
 muon_status muon_profile_enable(muon_handle h, int enable) {
@@ -529,9 +659,9 @@ muon_status muon_profile_collect(muon_handle h, muon_phase_times* out) {
 
 static muon_status check_single(muon_handle h, int64_t m, int64_t n) {
     if (!h) return MUON_ERR_INVALID_ARG;
-    const int T = gemm_tile_bf16();
+    const int T = gemm_tile_bf16(0);
     if (m < T || n < T || m % T || n % T || m > kMaxDim || n > kMaxDim) return MUON_ERR_INVALID_ARG;
-    if (upd_tile_m_bf16() != T || n % upd_tile_n_bf16()) return MUON_ERR_INVALID_ARG;
+    if (upd_tile_m_bf16(0) != T || n % upd_tile_n_bf16(0)) return MUON_ERR_INVALID_ARG;
     return MUON_OK;
 }
 

@@ -6,7 +6,9 @@
 //                    Newton-Schulz buffers, with zeros in the padding.
 //   norm_finalize    ||Y||_F from the per-tile partial sums (fixed order, so
 //                    every run gives the same bits) and s = 1/(||Y||_F + eps).
-//   apply_kernel     W <- (1 - lr wd) W - lr scale O.
+//   apply_kernel     W <- (1 - lr wd) W - lr scale O, then the optional
+//                    QK-Clip row scaling ("The Optimizer Wars ...", section
+//                    "What is MuonClip?").
 //   adamw_kernel     fused AdamW over a group of tensors.
 //
 // "About Muon: Why Not Adam" (kiungsong.github.io), section "The whole thing,
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
 
 template <bool VEC, bool NS_F32>
 __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity, float decay,
-                                           float step) {
+                                           float step, float qk_tau) {
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
     const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
     const int t = threadIdx.x;
@@ -277,8 +279,14 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
         if (valid[q] == 0) continue;
         const int64_t r = r0 + rr + 16 * q;
         const int64_t c = c0 + cg;
+        // QK-Clip: rows of head h scaled by sqrt(tau / S_max^h) when S_max^h > tau
+        float clip = 1.f;
+        if (d.qk_smax) {
+            const float sm = d.qk_smax[r / d.qk_block_rows];
+            clip = sm > qk_tau ? sqrtf(qk_tau / sm) : 1.f;
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[q].v[e] = decay * w[q].v[e] - sc * o[q][e];
+        for (int e = 0; e < 4; ++e) w[q].v[e] = clip * (decay * w[q].v[e] - sc * o[q][e]);
         store4<VEC>(d.param, pbf, r * d.ld_param + c, w[q], valid[q]);
         if (d.update_out) {
             Vals4 ov;
@@ -292,15 +300,16 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
 template <bool NS_F32>
 __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ descs, int n,
                                                     const int32_t* __restrict__ prefix,
-                                                    int parity, float decay, float step) {
+                                                    int parity, float decay, float step,
+                                                    float qk_tau) {
     const int tile = blockIdx.x;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
     if (d.vec4)
-        apply_tile<true, NS_F32>(d, lt, parity, decay, step);
+        apply_tile<true, NS_F32>(d, lt, parity, decay, step, qk_tau);
     else
-        apply_tile<false, NS_F32>(d, lt, parity, decay, step);
+        apply_tile<false, NS_F32>(d, lt, parity, decay, step, qk_tau);
 }
 
 // ---------------------------------------------------------------- AdamW ----
@@ -315,19 +324,23 @@ __device__ __forceinline__ void adamw_elem(float& th, float g, float& m, float& 
     th = th - lr * (mhat / (sqrtf(vhat) + eps) + wd * th);
 }
 
+__device__ __forceinline__ int adamw_tensor_of(const AdamwGroup& grp, int blk) {
+    int lo = 0, hi = grp.count - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (grp.block_prefix[mid] <= blk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// gscale: null, or a device scalar every gradient is multiplied by first
+// (global-norm clipping).
 __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, float b1, float b2,
                                                     float eps, float wd, float inv_bc1,
-                                                    float inv_bc2) {
+                                                    float inv_bc2, const float* gscale) {
     const int blk = blockIdx.x;
-    int ti = 0;
-    {
-        int lo = 0, hi = grp.count - 1;
-        while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (grp.block_prefix[mid] <= blk) lo = mid; else hi = mid - 1;
-        }
-        ti = lo;
-    }
+    const int ti = adamw_tensor_of(grp, blk);
+    const float gs = gscale ? gscale[0] : 1.f;
     const int64_t start = (int64_t)(blk - grp.block_prefix[ti]) * kAdamwChunk;
     const int64_t numel = grp.numel[ti];
     const int64_t end = start + kAdamwChunk < numel ? start + kAdamwChunk : numel;
@@ -342,6 +355,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
             const int64_t off = start + q * 1024 + threadIdx.x * 4;
             Vals4 th = load4<true>(P, pbf, off, 4);
             Vals4 g = load4<true>(G, gbf, off, 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g.v[e] *= gs;
             float4 m = ld_nt(M + off);
             float4 v = ld_nt(V + off);
             adamw_elem(th.v[0], g.v[0], m.x, v.x, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
@@ -356,8 +371,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
         for (int64_t i = start + threadIdx.x; i < end; i += 256) {
             float th = pbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P)[i])
                            : reinterpret_cast<const float*>(P)[i];
-            const float g = gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
-                                : reinterpret_cast<const float*>(G)[i];
+            const float g = gs * (gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
+                                      : reinterpret_cast<const float*>(G)[i]);
             float m = M[i], v = V[i];
             adamw_elem(th, g, m, v, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             if (pbf)
@@ -370,7 +385,61 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
     }
 }
 
+// Sum of squares of the gradients of one group, one partial per block of
+// kAdamwChunk elements, written at partials[block_offset + block].
+__global__ __launch_bounds__(256) void adamw_sumsq_kernel(AdamwGroup grp, float* partials,
+                                                          int block_offset) {
+    __shared__ float red[4];
+    const int blk = blockIdx.x;
+    const int ti = adamw_tensor_of(grp, blk);
+    const int64_t start = (int64_t)(blk - grp.block_prefix[ti]) * kAdamwChunk;
+    const int64_t numel = grp.numel[ti];
+    const int64_t end = start + kAdamwChunk < numel ? start + kAdamwChunk : numel;
+    const void* G = grp.grad[ti];
+    const int gbf = grp.grad_bf16[ti];
+    float ss = 0.f;
+    for (int64_t i = start + threadIdx.x; i < end; i += 256) {
+        const float g = gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
+                            : reinterpret_cast<const float*>(G)[i];
+        ss += g * g;
+    }
+    const float tot = block_sum_256(ss, red);
+    if (threadIdx.x == 0) partials[block_offset + blk] = tot;
+}
+
+// norm = sqrt(sum of partials) in a fixed order; scale = max_norm / norm if
+// norm > max_norm, else 1.
+__global__ __launch_bounds__(256) void clip_finalize_kernel(const float* partials, int nblocks,
+                                                            float max_norm, float* scale,
+                                                            float* norm_out) {
+    __shared__ double red[4];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < nblocks; i += 256) s += (double)partials[i];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const double norm = sqrt((red[0] + red[1]) + (red[2] + red[3]));
+        scale[0] = norm > (double)max_norm ? (float)((double)max_norm / norm) : 1.f;
+        if (norm_out) norm_out[0] = (float)norm;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_adamw_sumsq(const AdamwGroup& g, int total_blocks, float* partials,
+                              int block_offset, hipStream_t st) {
+    adamw_sumsq_kernel<<<total_blocks, 256, 0, st>>>(g, partials, block_offset);
+    return hipGetLastError();
+}
+
+hipError_t launch_clip_finalize(const float* partials, int nblocks, float max_norm, float* scale,
+                                float* norm_out, hipStream_t st) {
+    clip_finalize_kernel<<<1, 256, 0, st>>>(partials, nblocks, max_norm, scale, norm_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
                            int nesterov, int ns_f32, hipStream_t st) {
@@ -387,18 +456,20 @@ hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t 
 }
 
 hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
-                        float lr, float wd, int ns_f32, hipStream_t st) {
+                        float lr, float wd, float qk_tau, int ns_f32, hipStream_t st) {
     const float decay = 1.f - lr * wd;
     if (ns_f32)
-        apply_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr);
+        apply_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr, qk_tau);
     else
-        apply_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr);
+        apply_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr, qk_tau);
     return hipGetLastError();
 }
 
 hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,
-                        float eps, float wd, float bc1, float bc2, hipStream_t st) {
-    adamw_kernel<<<total_blocks, 256, 0, st>>>(g, lr, beta1, beta2, eps, wd, 1.f / bc1, 1.f / bc2);
+                        float eps, float wd, float bc1, float bc2, const float* gscale,
+                        hipStream_t st) {
+    adamw_kernel<<<total_blocks, 256, 0, st>>>(g, lr, beta1, beta2, eps, wd, 1.f / bc1, 1.f / bc2,
+                                               gscale);
     return hipGetLastError();
 }
 

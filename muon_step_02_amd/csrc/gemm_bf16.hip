@@ -401,27 +401,39 @@ inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
 
 using SymCfg = Cfg<256, 256, 2, 4>;
 using UpdCfg = Cfg<256, 256, 2, 4>;
+// matrices whose short side fits 128 (per-head blocks, small layers)
+using SmallCfg = Cfg<128, 128, 2, 2>;
 
 }  // namespace
 
-int gemm_tile_bf16() { return SymCfg::BM; }
-int upd_tile_m_bf16() { return UpdCfg::BM; }
-int upd_tile_n_bf16() { return UpdCfg::BN; }
+int gemm_tile_bf16(int small) { return small ? SmallCfg::BM : SymCfg::BM; }
+int upd_tile_m_bf16(int small) { return small ? SmallCfg::BM : UpdCfg::BM; }
+int upd_tile_n_bf16(int small) { return small ? SmallCfg::BN : UpdCfg::BN; }
 
-hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st) {
-    ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, int small,
+                            hipStream_t st) {
+    if (small)
+        ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
+    else
+        ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
     return hipGetLastError();
 }
 
 hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
-                            hipStream_t st) {
-    ns_sym_kernel<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
+                            int small, hipStream_t st) {
+    if (small)
+        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
+    else
+        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
     return hipGetLastError();
 }
 
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
-                              hipStream_t st) {
-    ns_update_kernel<UpdCfg><<<xcd_grid(total), UpdCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
+                              int small, hipStream_t st) {
+    if (small)
+        ns_update_kernel<SmallCfg><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
+    else
+        ns_update_kernel<UpdCfg><<<xcd_grid(total), UpdCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
     return hipGetLastError();
 }
 

@@ -15,8 +15,10 @@ namespace muon {
 // Canonical Newton-Schulz buffers are padded to these multiples so the GEMM
 // kernels run on whole tiles with no bounds checks.  The padding is zero and
 // the iteration keeps it zero: rows/cols of zeros stay zero under X X^T,
-// b A + c A A and a X + B X.
+// b A + c A A and a X + B X.  bf16 matrices whose short side is at most
+// kSmallBf16 use 128-wide tiles and padding ("small" class), the others 256.
 constexpr int kPadBf16 = 256;
+constexpr int kSmallBf16 = 128;
 constexpr int kPadF32 = 64;
 // Elementwise kernels (momentum, apply) work on 64 x 64 tiles of the weight.
 constexpr int kEwTile = 64;
@@ -30,6 +32,8 @@ struct MatDesc {
     float* mom;
     float* update_out;
     float* norm_out;
+    const float* qk_smax;   // optional: max attention logit per block of qk_block_rows rows
+    int64_t qk_block_rows;
     int64_t rows, cols;
     int64_t ld_param, ld_grad, ld_mom;
     int32_t param_dtype, grad_dtype;
@@ -88,19 +92,21 @@ hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, f
                            int nesterov, int ns_f32, hipStream_t st);
 hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t st);
 hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
-                        float lr, float wd, int ns_f32, hipStream_t st);
+                        float lr, float wd, float qk_tau, int ns_f32, hipStream_t st);
 
 // bf16 Newton-Schulz phases over all matrices.  `it` is the iteration index
 // (0-based): it selects the ping-pong buffers and, for it == 0, folds the
 // normalisation s = 1/(||Y||+eps) into the epilogues.
-hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
-hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+// `small` selects the 128-tile kernels for the small class.
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, int small,
                             hipStream_t st);
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+                            int small, hipStream_t st);
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
-                              hipStream_t st);
-int gemm_tile_bf16();  // square tile edge of the Gram/polynomial kernels
-int upd_tile_m_bf16();
-int upd_tile_n_bf16();
+                              int small, hipStream_t st);
+int gemm_tile_bf16(int small);  // square tile edge of the Gram/polynomial kernels
+int upd_tile_m_bf16(int small);
+int upd_tile_n_bf16(int small);
 
 hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
 hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
@@ -134,6 +140,11 @@ struct AdamwGroup {
 };
 constexpr int kAdamwChunk = 4096;  // elements per workgroup
 hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,
-                        float eps, float wd, float bc1, float bc2, hipStream_t st);
+                        float eps, float wd, float bc1, float bc2, const float* gscale,
+                        hipStream_t st);
+hipError_t launch_adamw_sumsq(const AdamwGroup& g, int total_blocks, float* partials,
+                              int block_offset, hipStream_t st);
+hipError_t launch_clip_finalize(const float* partials, int nblocks, float max_norm, float* scale,
+                                float* norm_out, hipStream_t st);
 
 }  // namespace muon

@@ -20,7 +20,7 @@ web page and the section on it:
 * "The Optimizer Wars: How Muon Is Replacing Adam in Frontier AI Training"
   (ai.info) -- section "What is Muon? Momentum orthogonalized by
   Newton-Schulz" (five quintic iterations, coefficients (3.4445, -4.7750,
-  2.0315)).
+  2.0315)) and section "What is MuonClip?" (QK-Clip after the update).
 * "Por qué AdamW para entrenar modelos de lenguaje, y qué está cambiando"
   (gustavoai.dev) -- sections "Momentum: recordar el paso anterior",
   "Adam: las dos ideas juntas", "La W: un error de regularización que duró
@@ -43,8 +43,9 @@ from .muon import (
     shape_scale,
     muon_matrix_step,
     muon_step,
+    qk_clip,
 )
-from .adamw import adamw_tensor_step, adamw_step
+from .adamw import adamw_tensor_step, adamw_step, clip_by_global_norm
 
 __all__ = [
     "MUON_COEFFS",
@@ -54,6 +55,8 @@ __all__ = [
     "shape_scale",
     "muon_matrix_step",
     "muon_step",
+    "qk_clip",
     "adamw_tensor_step",
     "adamw_step",
+    "clip_by_global_norm",
 ]

@@ -47,8 +47,25 @@ def adamw_tensor_step(theta, g, m, v, *, step, lr, beta1=0.9, beta2=0.95,
     return theta_new, m_new, v_new
 
 
-def adamw_step(params, grads, exp_avgs, exp_avg_sqs, **hparams):
-    """AdamW over a list of tensors (each independent).  Returns three lists."""
+def clip_by_global_norm(grads, max_norm):
+    """Gradient clipping to a global norm ("Por qué AdamW ...", section "Por
+    qué AdamW, y por qué con esos números": before the gradient enters m and
+    v, if its norm exceeds 1 it is rescaled to 1; the threshold is a
+    parameter here).  The norm is the Euclidean norm of all the given
+    tensors together.  Returns ``(clipped_grads, norm)``."""
+    gs = [np.asarray(g, dtype=np.float64) for g in grads]
+    norm = np.sqrt(sum(float(np.sum(g * g)) for g in gs))
+    if norm > max_norm:
+        gs = [g * (max_norm / norm) for g in gs]
+    return gs, norm
+
+
+def adamw_step(params, grads, exp_avgs, exp_avg_sqs, max_grad_norm=None, **hparams):
+    """AdamW over a list of tensors (each independent).  Returns three lists.
+    With ``max_grad_norm``, the gradients are first clipped together to that
+    global norm."""
+    if max_grad_norm is not None:
+        grads, _ = clip_by_global_norm(grads, max_grad_norm)
     ts, ms, vs = [], [], []
     for p, g, m, v in zip(params, grads, exp_avgs, exp_avg_sqs):
         t, mm, vv = adamw_tensor_step(p, g, m, v, **hparams)

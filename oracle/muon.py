@@ -125,9 +125,30 @@ def shape_scale(rows, cols, mode="moonlight"):
     raise ValueError("unknown scale mode %r" % (mode,))
 
 
+def qk_clip(W, s_max, tau, block_rows):
+    """QK-Clip of a query or key projection after its optimizer update.
+
+    "The Optimizer Wars ...", section "What is MuonClip? Kimi K2's fix for
+    exploding attention scores": for head h with maximum attention logit
+    ``S_max^h``, ``gamma_h = min(1, tau / S_max^h)``; the head's query and key
+    weights are each multiplied by ``sqrt(gamma_h)`` so their product, and the
+    logits, shrink by ``gamma_h``.  Here ``W`` holds the heads as consecutive
+    blocks of ``block_rows`` rows (PyTorch layout, one row per output
+    feature) and ``s_max[h]`` is head h's maximum logit.  A head whose
+    ``S_max`` does not exceed ``tau`` (including ``S_max <= 0``) is left alone.
+    """
+    W = _f64(W).copy()
+    s_max = np.asarray(s_max, dtype=np.float64).reshape(-1)
+    for h in range(s_max.size):
+        rows = slice(h * block_rows, min((h + 1) * block_rows, W.shape[0]))
+        if s_max[h] > tau:
+            W[rows] *= np.sqrt(tau / s_max[h])
+    return W
+
+
 def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
                      eps=1e-7, steps=5, coeffs=None, scale_mode="moonlight",
-                     extra_scale=1.0):
+                     extra_scale=1.0, qk_smax=None, qk_block_rows=0, qk_tau=100.0):
     """One Muon step for one weight matrix; returns ``(W_new, M_new, O)``.
 
     Order of operations ("About Muon: Why Not Adam", section "The whole thing,
@@ -140,7 +161,9 @@ def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
     4. ``s = shape_scale(rows, cols) * extra_scale`` (the extra factor is the
        starter configuration's extra scale knob, "Why Muon Works", 7.6);
     5. ``W <- (1 - lr*wd) W`` (decay uses the weight before the update), then
-       ``W <- W - lr * s * O``.
+       ``W <- W - lr * s * O``;
+    6. with ``qk_smax`` given, :func:`qk_clip` on the updated weight
+       (MuonClip: the clip follows the ordinary Muon update).
 
     ``O`` is the orthogonalised update before the multiplier, returned so
     tests can compare it directly.
@@ -153,6 +176,8 @@ def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
     s = shape_scale(rows, cols, scale_mode) * extra_scale
     W_new = (1.0 - lr * weight_decay) * W
     W_new = W_new - (lr * s) * O
+    if qk_smax is not None:
+        W_new = qk_clip(W_new, qk_smax, qk_tau, qk_block_rows)
     return W_new, M_new, O
 
 

@@ -405,3 +405,77 @@ def test_adamw_decay_uses_old_theta_and_step_validation():
     assert th[0] == pytest.approx(2.0 - 0.1 * (1.0 + 0.5 * 2.0), abs=1e-15)
     with pytest.raises(ValueError):
         oracle.adamw_tensor_step(th0, g, th0, th0, step=0, lr=0.1)
+
+
+# --------------------------------------------------------------------------
+# QK-Clip ("The Optimizer Wars ...", "What is MuonClip?") and gradient
+# clipping ("Por qué AdamW ...", "Por qué AdamW, y por qué con esos números")
+# --------------------------------------------------------------------------
+
+GOLD_QK = load_golden("qkclip_pages.txt")
+
+
+def test_qk_clip_caps_every_heads_max_logit_at_tau():
+    # Attention logits of head h are q.k with q = Wq_h x, k = Wk_h x'.
+    # Scaling both projections by sqrt(gamma_h) scales every logit by gamma_h,
+    # so after the clip each head's maximum is min(S_max^h, tau).
+    tau = GOLD_QK["tau_kimi_k2"][0]
+    rng = np.random.default_rng(12)
+    H, dh, dm, T = 4, 8, 32, 16
+    Wq = rng.standard_normal((H * dh, dm)) * 3.0
+    Wk = rng.standard_normal((H * dh, dm)) * 3.0
+    Wq[:dh] *= 0.05  # head 0 stays below tau
+    X = rng.standard_normal((T, dm))
+
+    def max_logits(q, k):
+        out = []
+        for h in range(H):
+            Q = X @ q[h * dh:(h + 1) * dh].T
+            K = X @ k[h * dh:(h + 1) * dh].T
+            out.append(np.max(Q @ K.T))
+        return np.array(out)
+
+    S = max_logits(Wq, Wk)
+    assert S[0] < tau and np.all(S[1:] > tau)
+    q2 = oracle.qk_clip(Wq, S, tau, dh)
+    k2 = oracle.qk_clip(Wk, S, tau, dh)
+    S2 = max_logits(q2, k2)
+    assert np.allclose(S2, np.minimum(S, tau), rtol=1e-12)
+    assert np.array_equal(q2[:dh], Wq[:dh])
+
+
+def test_qk_clip_is_a_post_update_row_scaling():
+    rng = np.random.default_rng(13)
+    W, G = rng.standard_normal((6, 5)), rng.standard_normal((6, 5))
+    smax = np.array([50.0, 400.0, 100.0])
+    Wn, Mn, O = oracle.muon_matrix_step(W, G, np.zeros_like(W), lr=0.1, weight_decay=0.1,
+                                        qk_smax=smax, qk_block_rows=2, qk_tau=100.0)
+    Wp, Mp, Op = oracle.muon_matrix_step(W, G, np.zeros_like(W), lr=0.1, weight_decay=0.1)
+    assert np.array_equal(Mn, Mp) and np.array_equal(O, Op)
+    assert np.allclose(Wn[0:2], Wp[0:2]) and np.allclose(Wn[4:6], Wp[4:6])
+    assert np.allclose(Wn[2:4], 0.5 * Wp[2:4])   # sqrt(100/400)
+
+
+def test_global_norm_clipping():
+    want, _ = GOLD_AD["grad_clip_threshold"]
+    rng = np.random.default_rng(14)
+    gs = [rng.standard_normal(7) * 3.0, rng.standard_normal((3, 4)) * 3.0]
+    norm = np.sqrt(sum(np.sum(g * g) for g in gs))
+    assert norm > want
+    cg, n = oracle.clip_by_global_norm(gs, want)
+    assert n == pytest.approx(norm)
+    assert np.sqrt(sum(np.sum(g * g) for g in cg)) == pytest.approx(want, rel=1e-12)
+    for a, b in zip(cg, gs):
+        assert np.allclose(a, b * want / norm)
+    small = [g * 1e-3 for g in gs]
+    cs, _ = oracle.clip_by_global_norm(small, want)
+    for a, b in zip(cs, small):
+        assert np.array_equal(a, b)
+    # clipping happens before the moments: second step with an unclipped g2
+    g1, g2 = np.array([30.0, 40.0]), np.array([0.3, -0.4])
+    ts, ms, vs = oracle.adamw_step([np.zeros(2)], [g1], [np.zeros(2)], [np.zeros(2)],
+                                   max_grad_norm=1.0, step=1, lr=1.0, weight_decay=0.0)
+    assert np.allclose(ms[0], 0.1 * g1 / 50.0)
+    ts, ms, vs = oracle.adamw_step(ts, [g2], ms, vs, max_grad_norm=1.0, step=2, lr=1.0,
+                                   weight_decay=0.0)
+    assert np.allclose(ms[0], 0.9 * 0.1 * g1 / 50.0 + 0.1 * g2)
