@@ -28,9 +28,8 @@
 // global->LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
 // staging) into two LDS stages, so the copy of slab k+1 overlaps the MFMAs
 // on slab k.  The epilogue goes through LDS so that every global access is a
-// coalesced 16-byte one.  An LDS row is 64 bf16 = 8 chunks of 16 bytes; chunk c of row r
-// lives at position c ^ (r & 7), so the 32 lanes of a fragment read (32
-// consecutive rows, one chunk) spread over all banks.
+// coalesced 16-byte one.  LDS rows are XOR-swizzled (see swz) so fragment
+// reads are free of bank conflicts.
 //
 // Grouped launch: one launch per phase covers every matrix; workgroup ->
 // (matrix, tile) through prefix sums of tiles per matrix.
@@ -46,46 +45,68 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 enum { GRAM = 0, POLY = 1, UPDATE = 2 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    static constexpr int BK = 64;
+    static constexpr int BK = BK_;   // k per LDS stage (32 or 64)
+    static constexpr int NS = NS_;   // LDS stages (2..4)
     static constexpr int NW = WM * WN;
     static constexpr int NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int CH = BK / 8;          // 16-byte chunks per LDS row
+    static constexpr int RPI = 64 / CH;        // rows per global_load_lds (1 KB)
     static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
-    static constexpr int LPS = ((BM + BN) / 8) / NW;  // slab copies per stage per wave
-    // epilogue: bands of RB rows staged as fp32 in one stage buffer
-    static constexpr int LDW = BN + 4;
-    static constexpr int RB = 32;
+    static constexpr int LPS = ((BM + BN) / RPI) / NW;  // slab copies per stage per wave
+    // epilogue: bands of RB rows staged as fp32 in one stage buffer; the row
+    // stride puts rows r and r + 4 (the two half-waves of an accumulator
+    // store) 32 banks apart
+    static constexpr int LDW = BN + 8;
+    static constexpr int RB = (32 * LDW * 4 <= STAGE * 2) ? 32 : 16;
     static_assert(RB * LDW * 4 <= STAGE * 2, "epilogue band must fit one stage");
+    static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 MFMA tile");
-    static_assert((BM / 8) % NW == 0 && (BN / 8) % NW == 0, "slab rows must split over waves");
+    static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "slab rows must split over waves");
     static_assert((RB * BN / 8) % NT == 0 && (BN * RB / 8) % NT == 0, "epilogue chunks must split");
 };
 
-// Copy rows [0, R) x k-chunk [0, 64) of a row-major bf16 operand (rows start
+// LDS slab layout: row r holds BK bf16 = CH chunks of 16 bytes; logical chunk
+// c of row r sits at chunk position c ^ swz(r).  A fragment read has 16
+// lanes per LDS cycle (16 x 16 B = all 64 banks) reading the same logical
+// chunk of 16 consecutive rows; 256 bytes hold 256 / (2 BK) rows, so the 16
+// reads are conflict-free iff (r mod rows-per-256B, position) differs
+// across them.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// Copy rows [0, R) x k-chunk [0, BK) of a row-major bf16 operand (rows start
 // at `g`, leading dimension ld) into an LDS slab, swizzled.  One
-// global_load_lds_dwordx4 moves 8 rows (1 KB); lane L fills physical chunk
-// L & 7 of row L >> 3, i.e. logical chunk (L & 7) ^ (L >> 3).
-template <int R, int NW>
+// global_load_lds_dwordx4 moves 1 KB (RPI rows, contiguous in LDS); lane L
+// fills chunk position L % CH of row L / CH, i.e. it fetches logical chunk
+// (L % CH) ^ swz(row).
+template <class C, int R>
 __device__ __forceinline__ void load_slab(const uint16_t* __restrict__ g, int64_t ld, uint16_t* slab,
                                           int wave, int lane) {
-    constexpr int PER_WAVE = (R / 8) / NW;
-    const int lrow = lane >> 3;
-    const int lch = (lane & 7) ^ lrow;
+    constexpr int PER_WAVE = (R / C::RPI) / C::NW;
+    const int lrow = lane / C::CH;
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
         const int grp = wave * PER_WAVE + q;
-        const uint16_t* src = g + (int64_t)(grp * 8 + lrow) * ld + lch * 8;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * 8 * 64), 16, 0, 0);
+        const int row = grp * C::RPI + lrow;
+        const int lch = (lane % C::CH) ^ swz<C::BK>(row);
+        const uint16_t* src = g + (int64_t)row * ld + lch * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * C::RPI * C::BK),
+                                         16, 0, 0);
     }
 }
 
+template <class C>
 __device__ __forceinline__ bf16x8 read_frag(const uint16_t* slab, int row, int lch) {
-    const int pch = lch ^ (row & 7);
-    return *reinterpret_cast<const bf16x8*>(slab + row * 64 + pch * 8);
+    const int pch = lch ^ swz<C::BK>(row);
+    return *reinterpret_cast<const bf16x8*>(slab + row * C::BK + pch * 8);
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -115,9 +136,9 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* sp, f32x16 (&acc)[C::
         const int lch = 2 * kk + khalf;
         bf16x8 a[C::FM], b[C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = read_frag(sp, wm * C::TM + i * 32 + frow, lch);
+        for (int i = 0; i < C::FM; ++i) a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = read_frag(sq, wn * C::TN + j * 32 + frow, lch);
+        for (int j = 0; j < C::FN; ++j) b[j] = read_frag<C>(sq, wn * C::TN + j * 32 + frow, lch);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -126,16 +147,33 @@ __device__ __forceinline__ void mfma_stage(const uint16_t* sp, f32x16 (&acc)[C::
     }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// The LDS stages.  Each is its own __shared__ variable (declared in the
+// kernel) so the compiler can tell that the copy into one stage does not
+// alias the fragment reads from another; otherwise it waits for every
+// outstanding copy before each read and the prefetch is lost.
+struct Stages {
+    uint16_t* s[4];
+};
+
+template <class C>
+__device__ __forceinline__ uint16_t* stage(const Stages& st, int i) {
+    return i == 0 ? st.s[0] : i == 1 ? st.s[1] : i == 2 ? st.s[2] : st.s[3];
+}
+
 // C tile = sum_k P[i][k] Q[j][k] for the BM rows starting at P0 and the BN
-// rows starting at Q0 (both leading dimension ld, K a multiple of 64), then
-// the epilogue.  s0 and s1 are the two LDS stages; they must be
-// distinct __shared__ variables so the compiler can tell that the copy into
-// one stage does not alias the fragment reads from the other (otherwise it
-// waits for every outstanding copy before each read and the prefetch is lost).
+// rows starting at Q0 (both leading dimension ld, K a multiple of BK), then
+// the epilogue.  NS-stage pipeline: the copy of slab k + NS - 1 is issued
+// while the MFMAs run on slab k.
 template <class C, bool HAS_E>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const uint16_t* __restrict__ Q0,
                                           int64_t ld, int K, int64_t row0, int64_t col0,
-                                          const Epi& ep, uint16_t* s0, uint16_t* s1) {
+                                          const Epi& ep, const Stages& st) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -151,22 +189,30 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int KT = K / C::BK;
-    load_slab<C::BM, C::NW>(P0, ld, s0, wave, lane);
-    load_slab<C::BN, C::NW>(Q0, ld, s0 + C::BM * C::BK, wave, lane);
-    for (int kt0 = 0; kt0 < KT; kt0 += 2) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < C::NS - 1; ++u) {
+        if (u < KT) {
+            uint16_t* dst = stage<C>(st, u);
+            load_slab<C, C::BM>(P0 + u * C::BK, ld, dst, wave, lane);
+            load_slab<C, C::BN>(Q0 + u * C::BK, ld, dst + C::BM * C::BK, wave, lane);
+        }
+    }
+    for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
+#pragma unroll
+        for (int u = 0; u < C::NS; ++u) {
             const int kt = kt0 + u;
             if (kt < KT) {
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of stage u landed
-                __syncthreads();                     // ... and every other wave's
-                if (kt + 1 < KT) {
-                    uint16_t* dst = u == 0 ? s1 : s0;
-                    const int64_t k0 = (int64_t)(kt + 1) * C::BK;
-                    load_slab<C::BM, C::NW>(P0 + k0, ld, dst, wave, lane);
-                    load_slab<C::BN, C::NW>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
+                // this wave's copies of slab kt have landed once at most the
+                // later slabs' copies are outstanding; then every wave's
+                if (kt + C::NS - 2 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
+                __syncthreads();
+                if (kt + C::NS - 1 < KT) {
+                    uint16_t* dst = stage<C>(st, (u + C::NS - 1) % C::NS);
+                    const int64_t k0 = (int64_t)(kt + C::NS - 1) * C::BK;
+                    load_slab<C, C::BM>(P0 + k0, ld, dst, wave, lane);
+                    load_slab<C, C::BN>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
                 }
-                mfma_stage<C>(u == 0 ? s0 : s1, acc, wm, wn, frow, khalf);
+                mfma_stage<C>(stage<C>(st, u), acc, wm, wn, frow, khalf);
             }
         }
     }
@@ -176,21 +222,40 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
     // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
     // combines 8 consecutive columns with E and stores 16 bytes of the output,
     // and, for the transposed copy, 8 consecutive rows of one column.
-    float* st = reinterpret_cast<float*>(s0);
+    float* sb = reinterpret_cast<float*>(st.s[0]);
 #pragma unroll 1
     for (int band = 0; band < C::BM / C::RB; ++band) {
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
-            const int fr0 = wm * C::TM + i * 32;
-            if (fr0 >= band * C::RB && fr0 < (band + 1) * C::RB) {
 #pragma unroll
-                for (int j = 0; j < C::FN; ++j) {
-                    const int c = wn * C::TN + j * 32 + frow;
+            for (int h = 0; h < 32 / C::RB + (C::RB > 32 ? 1 : 0); ++h) {
+                // fragment i covers tile rows [fr0, fr0 + 32); with RB = 16
+                // it spans two bands (register groups r >> 2 in {0,1} / {2,3})
+                const int fr0 = wm * C::TM + i * 32;
+                if (C::RB == 32) {
+                    if (fr0 == band * C::RB) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int rr = fr0 - band * C::RB + 8 * (r >> 2) + 4 * khalf + (r & 3);
-                        st[rr * C::LDW + c] = acc[i][j][r];
+                        for (int j = 0; j < C::FN; ++j) {
+                            const int c = wn * C::TN + j * 32 + frow;
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3);
+                                sb[rr * C::LDW + c] = acc[i][j][r];
+                            }
+                        }
+                    }
+                } else {
+                    if (fr0 + 16 * h == band * C::RB) {
+#pragma unroll
+                        for (int j = 0; j < C::FN; ++j) {
+                            const int c = wn * C::TN + j * 32 + frow;
+#pragma unroll
+                            for (int r = 8 * h; r < 8 * h + 8; ++r) {
+                                const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3) - 16 * h;
+                                sb[rr * C::LDW + c] = acc[i][j][r];
+                            }
+                        }
                     }
                 }
             }
@@ -201,8 +266,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
         for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
             const int ch = q * C::NT + threadIdx.x;
             const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
-            const float4 a0 = *reinterpret_cast<const float4*>(st + rr * C::LDW + c8);
-            const float4 a1 = *reinterpret_cast<const float4*>(st + rr * C::LDW + c8 + 4);
+            const float4 a0 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8);
+            const float4 a1 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8 + 4);
             float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             if (HAS_E) {
                 const uint4 ev = *reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8);
@@ -224,8 +289,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
             o.w = pack2(v[6], v[7]);
             *reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8) = o;
             if (ep.outT) {
-                *reinterpret_cast<float4*>(st + rr * C::LDW + c8) = make_float4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<float4*>(st + rr * C::LDW + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                *reinterpret_cast<float4*>(sb + rr * C::LDW + c8) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(sb + rr * C::LDW + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
             }
         }
         if (ep.outT) {
@@ -236,7 +301,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
                 const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = st[(i8 + e) * C::LDW + c];
+                for (int e = 0; e < 8; ++e) v[e] = sb[(i8 + e) * C::LDW + c];
                 uint4 o;
                 o.x = pack2(v[0], v[1]);
                 o.y = pack2(v[2], v[3]);
@@ -284,8 +349,11 @@ template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict__ descs, int n,
                                                        const int32_t* __restrict__ prefix, int total,
                                                        int it, float cb, float cc) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    const Stages st{{lds0, lds1, lds2, lds3}};
     const int tile = xcd_tile(total);
     if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
@@ -319,15 +387,18 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, s0, s1);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
 }
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
                                                           const int32_t* __restrict__ prefix,
                                                           int total, int it, float ca) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    const Stages st{{lds0, lds1, lds2, lds3}};
     const int tile = xcd_tile(total);
     if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
@@ -349,16 +420,19 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     ep.coef_acc = 1.f;
     ep.post = (it == 0) ? d.inv_norm[0] : 1.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, s0, s1);
+    gemm_tile<C, true>(B + r0 * mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, st);
 }
 
 // single-matrix variants for the test hooks
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
                                                        int K, uint16_t* out, int64_t ld_out,
-                                                       float s2, float cb, float cc, int total) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+                                                       float sq, float cb, float cc, int total) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    const Stages st{{lds0, lds1, lds2, lds3}};
     const int tile = xcd_tile(total);
     if (tile < 0) return;
     int ti, tj;
@@ -369,12 +443,12 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
     ep.outT = (ti != tj) ? out : nullptr;
     ep.ld_outT = ld_out;
     if (PHASE == GRAM) {
-        ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = s2; ep.post = 1.f;
+        ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = sq; ep.post = 1.f;
     } else {
         ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, K, r0, c0, ep, s0, s1);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, K, r0, c0, ep, st);
 }
 
 template <class C>
@@ -384,8 +458,11 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
                                                           uint16_t* Xo, uint16_t* XoT, int m,
                                                           int n, int64_t ldx, int64_t ldb, float ca,
                                                           float s, int total) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t s1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    const Stages st{{lds0, lds1, lds2, lds3}};
     const int tile = xcd_tile(total);
     if (tile < 0) return;
     int ti, tj;
@@ -394,7 +471,7 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     ep.out = Xo; ep.ld_out = ldx; ep.outT = XoT; ep.ld_outT = ldb;
     ep.E = X; ep.ld_e = ldx; ep.coef_e = ca; ep.coef_acc = 1.f; ep.post = s;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, s0, s1);
+    gemm_tile<C, true>(B + r0 * ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, st);
 }
 
 inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
