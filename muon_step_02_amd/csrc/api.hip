@@ -153,6 +153,7 @@ struct ClassPlan {
     std::vector<int32_t> pgram, pupd;   // count + 1 entries each
     size_t off_pgram = 0, off_pupd = 0;
     int total_gram = 0, total_upd = 0;
+    XcdSplit xs_gram, xs_poly, xs_upd;  // per-XCD tile ranges of equal work
 };
 
 struct Plan {
@@ -256,8 +257,22 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
     }
     P.total_ew = (int)tew;
     for (int c = 0; c < 2; ++c) {
-        P.cls[c].total_gram = (int)tgram[c];
-        P.cls[c].total_upd = (int)tupd[c];
+        ClassPlan& C = P.cls[c];
+        C.total_gram = (int)tgram[c];
+        C.total_upd = (int)tupd[c];
+        // tile work = k-steps: the Gram runs over n', the polynomial and the
+        // update over m'
+        std::vector<int32_t> tg(C.count), tu(C.count);
+        std::vector<int64_t> wn(C.count), wm(C.count);
+        for (int k = 0; k < C.count; ++k) {
+            tg[k] = C.pgram[k + 1] - C.pgram[k];
+            tu[k] = C.pupd[k + 1] - C.pupd[k];
+            wn[k] = P.d[C.first + k].np;
+            wm[k] = P.d[C.first + k].mp;
+        }
+        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count);
+        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count);
+        C.xs_upd = xcd_split(tu.data(), wm.data(), C.count);
     }
 
     size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
@@ -467,19 +482,19 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 2, s, [&] { return launch_gram_bf16(dc, C.count, pc[k], C.total_gram, it, k, s); });
+            e = timed(h, 2, s, [&] { return launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k, s); });
         }
         for (int k = 0; k < 2 && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.total_gram, b, c, k, s); });
+            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, b, c, k, s); });
         }
         for (int k = 0; k < 2 && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.total_upd, it, a, k, s); });
+            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, a, k, s); });
         }
     }
     if (e == hipSuccess)

@@ -313,15 +313,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
     }
 }
 
-// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
-// b % 8).  Renumbering b -> (b % 8) * per + b / 8 gives each XCD a contiguous
-// range of tiles, so the tiles sharing operand slabs share one L2.  The grid
-// is 8 * per workgroups; numbers past `total` exit.
-__device__ __forceinline__ int xcd_tile(int total) {
-    const int per = (int)(gridDim.x >> 3);
+// Tile of this workgroup under an XcdSplit (-1: none, exit).
+__device__ __forceinline__ int xcd_tile(const XcdSplit& xs) {
     const int b = (int)blockIdx.x;
-    const int t = (b & 7) * per + (b >> 3);
-    return t < total ? t : -1;
+    const int x = b & 7;
+    const int t = xs.b[x] + (b >> 3);
+    return t < xs.b[x + 1] ? t : -1;
 }
 
 __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
@@ -347,14 +344,14 @@ __device__ __forceinline__ void grouped_index(int lt, int trows, int tcols, int&
 // Gram and polynomial: SYRK-like over the lower triangle of tiles.
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict__ descs, int n,
-                                                       const int32_t* __restrict__ prefix, int total,
-                                                       int it, float cb, float cc) {
+                                                       const int32_t* __restrict__ prefix,
+                                                       XcdSplit xs, int it, float cb, float cc) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(total);
+    const int tile = xcd_tile(xs);
     if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
@@ -393,13 +390,13 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
 template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
                                                           const int32_t* __restrict__ prefix,
-                                                          int total, int it, float ca) {
+                                                          XcdSplit xs, int it, float ca) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(total);
+    const int tile = xcd_tile(xs);
     if (tile < 0) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
@@ -427,13 +424,13 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
                                                        int K, uint16_t* out, int64_t ld_out,
-                                                       float sq, float cb, float cc, int total) {
+                                                       float sq, float cb, float cc, XcdSplit xs) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(total);
+    const int tile = xcd_tile(xs);
     if (tile < 0) return;
     int ti, tj;
     tri_index(tile, ti, tj);
@@ -457,13 +454,13 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* Xo, uint16_t* XoT, int m,
                                                           int n, int64_t ldx, int64_t ldb, float ca,
-                                                          float s, int total) {
+                                                          float s, XcdSplit xs) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(total);
+    const int tile = xcd_tile(xs);
     if (tile < 0) return;
     int ti, tj;
     grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
@@ -474,7 +471,7 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     gemm_tile<C, true>(B + r0 * ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, st);
 }
 
-inline int xcd_grid(int total) { return ((total + 7) / 8) * 8; }
+inline int xcd_grid(const XcdSplit& xs) { return 8 * (xs.per > 0 ? xs.per : 1); }
 
 using SymCfg = Cfg<256, 256, 2, 4>;
 using UpdCfg = Cfg<256, 256, 2, 4>;
@@ -487,50 +484,88 @@ int gemm_tile_bf16(int small) { return small ? SmallCfg::BM : SymCfg::BM; }
 int upd_tile_m_bf16(int small) { return small ? SmallCfg::BM : UpdCfg::BM; }
 int upd_tile_n_bf16(int small) { return small ? SmallCfg::BN : UpdCfg::BN; }
 
-hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, int small,
-                            hipStream_t st) {
-    if (small)
-        ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
-    else
-        ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, it, 0.f, 0.f);
-    return hipGetLastError();
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n) {
+    XcdSplit xs;
+    int64_t total_w = 0, total_t = 0;
+    for (int k = 0; k < n; ++k) {
+        total_w += (int64_t)ntiles[k] * weight[k];
+        total_t += ntiles[k];
+    }
+    // boundary x: first tile whose preceding work reaches x/8 of the total
+    xs.b[0] = 0;
+    int x = 1;
+    int64_t cum_w = 0, cum_t = 0;
+    for (int k = 0; k < n && x < 8; ++k) {
+        const int64_t w = weight[k] > 0 ? weight[k] : 1;
+        const int64_t end_w = cum_w + (int64_t)ntiles[k] * w;
+        while (x < 8 && end_w * 8 >= (int64_t)x * total_w) {
+            // smallest t in [0, ntiles] with (cum_w + t*w) * 8 >= x * total_w
+            const int64_t need = (int64_t)x * total_w - cum_w * 8;
+            int64_t t = need <= 0 ? 0 : (need + 8 * w - 1) / (8 * w);
+            if (t > ntiles[k]) t = ntiles[k];
+            xs.b[x++] = (int32_t)(cum_t + t);
+        }
+        cum_w = end_w;
+        cum_t += ntiles[k];
+    }
+    while (x < 9) xs.b[x++] = (int32_t)total_t;
+    xs.b[8] = (int32_t)total_t;
+    xs.per = 0;
+    for (int i = 0; i < 8; ++i) {
+        if (xs.b[i + 1] < xs.b[i]) xs.b[i + 1] = xs.b[i];
+        if (xs.b[i + 1] - xs.b[i] > xs.per) xs.per = xs.b[i + 1] - xs.b[i];
+    }
+    return xs;
 }
 
-hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st) {
     if (small)
-        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
+        ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f);
     else
-        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(d, n, p.gram, total, 0, b, c);
+        ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f);
     return hipGetLastError();
 }
 
-hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
-                              int small, hipStream_t st) {
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float b,
+                            float c, int small, hipStream_t st) {
     if (small)
-        ns_update_kernel<SmallCfg><<<xcd_grid(total), SmallCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
+        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, b, c);
     else
-        ns_update_kernel<UpdCfg><<<xcd_grid(total), UpdCfg::NT, 0, st>>>(d, n, p.upd, total, it, a);
+        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, b, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
+                              float a, int small, hipStream_t st) {
+    if (small)
+        ns_update_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.upd, xs, it, a);
+    else
+        ns_update_kernel<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(d, n, p.upd, xs, it, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
                                    float s2, hipStream_t st) {
     const int T = m / SymCfg::BM;
-    const int total = T * (T + 1) / 2;
-    ns_sym_single<SymCfg, GRAM><<<xcd_grid(total), SymCfg::NT, 0, st>>>(
+    const int32_t total = T * (T + 1) / 2;
+    const int64_t w = 1;
+    const XcdSplit xs = xcd_split(&total, &w, 1);
+    ns_sym_single<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), ldx, n, reinterpret_cast<uint16_t*>(A), lda, s2, 0.f,
-        0.f, total);
+        0.f, xs);
     return hipGetLastError();
 }
 
 hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
                                    hipStream_t st) {
     const int T = m / SymCfg::BM;
-    const int total = T * (T + 1) / 2;
-    ns_sym_single<SymCfg, POLY><<<xcd_grid(total), SymCfg::NT, 0, st>>>(
+    const int32_t total = T * (T + 1) / 2;
+    const int64_t w = 1;
+    const XcdSplit xs = xcd_split(&total, &w, 1);
+    ns_sym_single<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, b,
-        c, total);
+        c, xs);
     return hipGetLastError();
 }
 
@@ -538,10 +573,13 @@ hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* 
                                      void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
                                      float s, hipStream_t st) {
     const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
-    ns_update_single<UpdCfg><<<xcd_grid(tiles), UpdCfg::NT, 0, st>>>(
+    const int32_t total = tiles;
+    const int64_t w = 1;
+    const XcdSplit xs = xcd_split(&total, &w, 1);
+    ns_update_single<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(XT),
         reinterpret_cast<const uint16_t*>(B), reinterpret_cast<uint16_t*>(Xo),
-        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s, tiles);
+        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s, xs);
     return hipGetLastError();
 }
 

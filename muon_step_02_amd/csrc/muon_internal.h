@@ -98,12 +98,25 @@ hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int 
 // (0-based): it selects the ping-pong buffers and, for it == 0, folds the
 // normalisation s = 1/(||Y||+eps) into the epilogues.
 // `small` selects the 128-tile kernels for the small class.
-hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, int total, int it, int small,
-                            hipStream_t st);
-hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+//
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  XcdSplit gives XCD x the contiguous tile range [b[x], b[x+1]):
+// tiles that share operand slabs then share one L2, and the ranges are cut
+// at equal work (tiles weighted by their K), not equal tile counts.  The
+// grid is 8 * per workgroups, per = the largest range.
+struct XcdSplit {
+    int32_t b[9];
+    int32_t per;
+};
+// Split `ntiles[k]` tiles of weight `weight[k]` (matrix order) into 8 ranges.
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n);
+
+hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st);
-hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, int total, int it, float a,
-                              int small, hipStream_t st);
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float b,
+                            float c, int small, hipStream_t st);
+hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
+                              float a, int small, hipStream_t st);
 int gemm_tile_bf16(int small);  // square tile edge of the Gram/polynomial kernels
 int upd_tile_m_bf16(int small);
 int upd_tile_n_bf16(int small);

@@ -172,3 +172,57 @@ def test_workload_shapes_and_flops():
     n_params = sum(int(np.prod(t.shape)) for t in c4.tensors)
     assert n_params == pytest.approx(1.415e9, rel=1e-3)
     assert sum(int(np.prod(c4.tensors[i].shape)) for i in c4.adamw) == pytest.approx(206.6e6, rel=2e-3)
+
+
+XCD_SPLIT_TEST = r"""
+#include <cstdio>
+#include <cstdint>
+#include <cstdlib>
+#include <vector>
+#include <algorithm>
+namespace muon {
+struct XcdSplit { int32_t b[9]; int32_t per; };
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n);
+}
+int main() {
+    srand(7);
+    for (int trial = 0; trial < 20000; ++trial) {
+        int n = 1 + rand() % 12;
+        std::vector<int32_t> t(n);
+        std::vector<int64_t> w(n);
+        int64_t total_t = 0, total_w = 0, wmax = 0;
+        for (int k = 0; k < n; ++k) {
+            t[k] = (trial % 3 == 0) ? rand() % 3 : 1 + rand() % 300;
+            w[k] = 1 + rand() % 256;
+            total_t += t[k]; total_w += t[k] * w[k]; wmax = std::max(wmax, w[k]);
+        }
+        muon::XcdSplit xs = muon::xcd_split(t.data(), w.data(), n);
+        if (xs.b[0] != 0 || xs.b[8] != total_t) { printf("bad ends %d\n", trial); return 1; }
+        int per = 0;
+        for (int x = 0; x < 8; ++x) {
+            if (xs.b[x + 1] < xs.b[x]) { printf("not monotone %d\n", trial); return 1; }
+            per = std::max(per, xs.b[x + 1] - xs.b[x]);
+        }
+        if (per != xs.per) { printf("per %d\n", trial); return 1; }
+        // work of each range within one tile of the ideal eighth
+        std::vector<int64_t> tw; for (int k = 0; k < n; ++k) for (int i = 0; i < t[k]; ++i) tw.push_back(w[k]);
+        for (int x = 0; x < 8; ++x) {
+            int64_t s = 0; for (int i = xs.b[x]; i < xs.b[x + 1]; ++i) s += tw[i];
+            if (s * 8 > total_w + 8 * wmax) { printf("unbalanced %d x=%d %lld/%lld\n", trial, x, (long long)s, (long long)total_w); return 1; }
+        }
+    }
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+def test_xcd_split_covers_every_tile_once_with_balanced_work(tmp_path):
+    src = tmp_path / "xs.cpp"
+    src.write_text(XCD_SPLIT_TEST)
+    exe = tmp_path / "xs"
+    libdir = os.path.dirname(mu.LIB_PATH)
+    subprocess.run(["g++", "-O1", str(src), "-o", str(exe), "-L" + libdir, "-lmuon",
+                    "-Wl,-rpath," + libdir], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
