@@ -39,20 +39,20 @@ typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 // Streaming accesses: every element of the optimizer's tensors is touched
 // once per kernel, so loads and stores bypass cache retention.
 __device__ __forceinline__ float4 ld_nt(const float* p) {
-    const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    const f32x4v t = __builtin_nontemporal_load((const MUON_GLOBAL f32x4v*)p);
     return make_float4(t.x, t.y, t.z, t.w);
 }
 __device__ __forceinline__ void st_nt(float* p, float4 v) {
     const f32x4v t = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(t, reinterpret_cast<f32x4v*>(p));
+    __builtin_nontemporal_store(t, (MUON_GLOBAL f32x4v*)p);
 }
 __device__ __forceinline__ uint2 ld_nt(const uint16_t* p) {
-    const u32x2v t = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+    const u32x2v t = __builtin_nontemporal_load((const MUON_GLOBAL u32x2v*)p);
     return make_uint2(t.x, t.y);
 }
 __device__ __forceinline__ void st_nt(uint16_t* p, uint2 v) {
     const u32x2v t = {v.x, v.y};
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x2v*>(p));
+    __builtin_nontemporal_store(t, (MUON_GLOBAL u32x2v*)p);
 }
 
 template <bool VEC>
@@ -74,8 +74,8 @@ __device__ __forceinline__ Vals4 load4(const void* base, int dtype_bf16, int64_t
         for (int e = 0; e < 4; ++e) {
             if (e < valid) {
                 r.v[e] = dtype_bf16
-                    ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[off + e])
-                    : reinterpret_cast<const float*>(base)[off + e];
+                    ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(base) + off + e))
+                    : gld(reinterpret_cast<const float*>(base) + off + e);
             } else {
                 r.v[e] = 0.f;
             }
@@ -101,9 +101,9 @@ __device__ __forceinline__ void store4(void* base, int dtype_bf16, int64_t off, 
         for (int e = 0; e < 4; ++e) {
             if (e < valid) {
                 if (dtype_bf16)
-                    reinterpret_cast<uint16_t*>(base)[off + e] = f32_to_bf16_bits(r.v[e]);
+                    gst(reinterpret_cast<uint16_t*>(base) + off + e, f32_to_bf16_bits(r.v[e]));
                 else
-                    reinterpret_cast<float*>(base)[off + e] = r.v[e];
+                    gst(reinterpret_cast<float*>(base) + off + e, r.v[e]);
             }
         }
     }
@@ -113,13 +113,13 @@ __device__ __forceinline__ void store4(void* base, int dtype_bf16, int64_t off, 
 template <bool NS_F32>
 __device__ __forceinline__ void store_ns4(void* base, int64_t off, const float* v) {
     if (NS_F32) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) =
-            make_float4(v[0], v[1], v[2], v[3]);
+        gst(reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off),
+            make_float4(v[0], v[1], v[2], v[3]));
     } else {
         uint2 u;
         u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
         u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = u;
+        gst(reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off), u);
     }
 }
 
@@ -208,7 +208,7 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
         store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cg, v);
     }
     const float tot = block_sum_256(ss, red);
-    if (threadIdx.x == 0) d.partials[lt] = tot;
+    if (threadIdx.x == 0) gst(d.partials + lt, tot);
 }
 
 template <bool NS_F32>
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
     const MatDesc& d = descs[blockIdx.x];
     __shared__ double red[4];
     double s = 0.0;
-    for (int i = threadIdx.x; i < d.ew_tiles; i += 256) s += (double)d.partials[i];
+    for (int i = threadIdx.x; i < d.ew_tiles; i += 256) s += (double)gld(d.partials + i);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
     if (threadIdx.x == 0) {
         const double tot = (red[0] + red[1]) + (red[2] + red[3]);
         const double nu = sqrt(tot);
-        d.inv_norm[0] = (float)(1.0 / (nu + (double)eps));
-        if (d.norm_out) d.norm_out[0] = (float)nu;
+        gst(d.inv_norm, (float)(1.0 / (nu + (double)eps)));
+        if (d.norm_out) gst(d.norm_out, (float)nu);
     }
 }
 
@@ -282,7 +282,7 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
         // QK-Clip: rows of head h scaled by sqrt(tau / S_max^h) when S_max^h > tau
         float clip = 1.f;
         if (d.qk_smax) {
-            const float sm = d.qk_smax[r / d.qk_block_rows];
+            const float sm = gld(d.qk_smax + r / d.qk_block_rows);
             clip = sm > qk_tau ? sqrtf(qk_tau / sm) : 1.f;
         }
 #pragma unroll
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
                                                     float inv_bc2, const float* gscale) {
     const int blk = blockIdx.x;
     const int ti = adamw_tensor_of(grp, blk);
-    const float gs = gscale ? gscale[0] : 1.f;
+    const float gs = gscale ? gld(gscale) : 1.f;
     const int64_t start = (int64_t)(blk - grp.block_prefix[ti]) * kAdamwChunk;
     const int64_t numel = grp.numel[ti];
     const int64_t end = start + kAdamwChunk < numel ? start + kAdamwChunk : numel;
@@ -369,18 +369,18 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
         }
     } else {
         for (int64_t i = start + threadIdx.x; i < end; i += 256) {
-            float th = pbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(P)[i])
-                           : reinterpret_cast<const float*>(P)[i];
-            const float g = gs * (gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
-                                      : reinterpret_cast<const float*>(G)[i]);
-            float m = M[i], v = V[i];
+            float th = pbf ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(P) + i))
+                           : gld(reinterpret_cast<const float*>(P) + i);
+            const float g = gs * (gbf ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(G) + i))
+                                      : gld(reinterpret_cast<const float*>(G) + i));
+            float m = gld(M + i), v = gld(V + i);
             adamw_elem(th, g, m, v, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
             if (pbf)
-                reinterpret_cast<uint16_t*>(P)[i] = f32_to_bf16_bits(th);
+                gst(reinterpret_cast<uint16_t*>(P) + i, f32_to_bf16_bits(th));
             else
-                reinterpret_cast<float*>(P)[i] = th;
-            M[i] = m;
-            V[i] = v;
+                gst(reinterpret_cast<float*>(P) + i, th);
+            gst(M + i, m);
+            gst(V + i, v);
         }
     }
 }
@@ -399,12 +399,12 @@ __global__ __launch_bounds__(256) void adamw_sumsq_kernel(AdamwGroup grp, float*
     const int gbf = grp.grad_bf16[ti];
     float ss = 0.f;
     for (int64_t i = start + threadIdx.x; i < end; i += 256) {
-        const float g = gbf ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(G)[i])
-                            : reinterpret_cast<const float*>(G)[i];
+        const float g = gbf ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(G) + i))
+                            : gld(reinterpret_cast<const float*>(G) + i);
         ss += g * g;
     }
     const float tot = block_sum_256(ss, red);
-    if (threadIdx.x == 0) partials[block_offset + blk] = tot;
+    if (threadIdx.x == 0) gst(partials + block_offset + blk, tot);
 }
 
 // norm = sqrt(sum of partials) in a fixed order; scale = max_norm / norm if
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void clip_finalize_kernel(const float* partial
                                                             float* norm_out) {
     __shared__ double red[4];
     double s = 0.0;
-    for (int i = threadIdx.x; i < nblocks; i += 256) s += (double)partials[i];
+    for (int i = threadIdx.x; i < nblocks; i += 256) s += (double)gld(partials + i);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -422,8 +422,8 @@ __global__ __launch_bounds__(256) void clip_finalize_kernel(const float* partial
     __syncthreads();
     if (threadIdx.x == 0) {
         const double norm = sqrt((red[0] + red[1]) + (red[2] + red[3]));
-        scale[0] = norm > (double)max_norm ? (float)((double)max_norm / norm) : 1.f;
-        if (norm_out) norm_out[0] = (float)norm;
+        gst(scale, norm > (double)max_norm ? (float)((double)max_norm / norm) : 1.f);
+        if (norm_out) gst(norm_out, (float)norm);
     }
 }
 

@@ -270,7 +270,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
             const float4 a1 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8 + 4);
             float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             if (HAS_E) {
-                const uint4 ev = *reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8);
+                const uint4 ev = gld(reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8));
                 const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -287,7 +287,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
             o.y = pack2(v[2], v[3]);
             o.z = pack2(v[4], v[5]);
             o.w = pack2(v[6], v[7]);
-            *reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8) = o;
+            gst(reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8), o);
             if (ep.outT) {
                 *reinterpret_cast<float4*>(sb + rr * C::LDW + c8) = make_float4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<float4*>(sb + rr * C::LDW + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -307,7 +307,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
                 o.y = pack2(v[2], v[3]);
                 o.z = pack2(v[4], v[5]);
                 o.w = pack2(v[6], v[7]);
-                *reinterpret_cast<uint4*>(ep.outT + (col0 + c) * ep.ld_outT + brow + i8) = o;
+                gst(reinterpret_cast<uint4*>(ep.outT + (col0 + c) * ep.ld_outT + brow + i8), o);
             }
         }
     }
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
     if (PHASE == GRAM) {
         src = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
         ld = np;
-        const float s = (it == 0) ? d.inv_norm[0] : 1.f;
+        const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
         ep.E = nullptr;
         ep.ld_e = 0;
         ep.coef_e = 0.f;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     ep.ld_e = np;
     ep.coef_e = ca;
     ep.coef_acc = 1.f;
-    ep.post = (it == 0) ? d.inv_norm[0] : 1.f;
+    ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
     gemm_tile<C, true>(B + r0 * mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, st);
 }

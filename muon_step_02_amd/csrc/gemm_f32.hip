@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__
         for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
 
     for (int k0 = 0; k0 < K; k0 += KS) {
-        const float4 pv = *reinterpret_cast<const float4*>(Pr + k0);
-        const float4 qv = *reinterpret_cast<const float4*>(Qr + k0);
+        const float4 pv = gld(reinterpret_cast<const float4*>(Pr + k0));
+        const float4 qv = gld(reinterpret_cast<const float4*>(Qr + k0));
         __syncthreads();
         Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
         Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
@@ -91,43 +91,43 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__
     const int64_t i0 = (int64_t)ti * T + ty * 4;
     const int64_t j0 = (int64_t)tj * T + tx * 4;
     if (PHASE == GRAM) {
-        const float s = (it == 0) ? d.inv_norm[0] : 1.f;
+        const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
         const float s2 = s * s;
         float* A = reinterpret_cast<float*>(d.a);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<float4*>(A + (i0 + r) * mp + j0) =
-                make_float4(s2 * acc[r][0], s2 * acc[r][1], s2 * acc[r][2], s2 * acc[r][3]);
+            gst(reinterpret_cast<float4*>(A + (i0 + r) * mp + j0),
+                make_float4(s2 * acc[r][0], s2 * acc[r][1], s2 * acc[r][2], s2 * acc[r][3]));
     } else if (PHASE == POLY) {
         const float* A = reinterpret_cast<const float*>(d.a);
         float* B = reinterpret_cast<float*>(d.b);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float4 e = *reinterpret_cast<const float4*>(A + (i0 + r) * mp + j0);
-            *reinterpret_cast<float4*>(B + (i0 + r) * mp + j0) =
+            const float4 e = gld(reinterpret_cast<const float4*>(A + (i0 + r) * mp + j0));
+            gst(reinterpret_cast<float4*>(B + (i0 + r) * mp + j0),
                 make_float4(cb * e.x + cc * acc[r][0], cb * e.y + cc * acc[r][1],
-                            cb * e.z + cc * acc[r][2], cb * e.w + cc * acc[r][3]);
+                            cb * e.z + cc * acc[r][2], cb * e.w + cc * acc[r][3]));
         }
     } else {
-        const float post = (it == 0) ? d.inv_norm[0] : 1.f;
+        const float post = (it == 0) ? gld(d.inv_norm) : 1.f;
         const float* X = reinterpret_cast<const float*>(d.x[it & 1]);
         float* Xo = reinterpret_cast<float*>(d.x[(it + 1) & 1]);
         float* XoT = reinterpret_cast<float*>(d.xt[(it + 1) & 1]);
         float v[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float4 e = *reinterpret_cast<const float4*>(X + (i0 + r) * np + j0);
+            const float4 e = gld(reinterpret_cast<const float4*>(X + (i0 + r) * np + j0));
             v[r][0] = post * (ca * e.x + acc[r][0]);
             v[r][1] = post * (ca * e.y + acc[r][1]);
             v[r][2] = post * (ca * e.z + acc[r][2]);
             v[r][3] = post * (ca * e.w + acc[r][3]);
-            *reinterpret_cast<float4*>(Xo + (i0 + r) * np + j0) =
-                make_float4(v[r][0], v[r][1], v[r][2], v[r][3]);
+            gst(reinterpret_cast<float4*>(Xo + (i0 + r) * np + j0),
+                make_float4(v[r][0], v[r][1], v[r][2], v[r][3]));
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            *reinterpret_cast<float4*>(XoT + (j0 + c) * mp + i0) =
-                make_float4(v[0][c], v[1][c], v[2][c], v[3][c]);
+            gst(reinterpret_cast<float4*>(XoT + (j0 + c) * mp + i0),
+                make_float4(v[0][c], v[1][c], v[2][c], v[3][c]));
     }
 }
 

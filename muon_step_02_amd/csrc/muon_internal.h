@@ -12,6 +12,29 @@
 
 namespace muon {
 
+// ---- global-memory accessors ----------------------------------------------
+// Pointers that reach a kernel through a descriptor are generic, and a plain
+// dereference compiles to a flat_* instruction.  Flat accesses count against
+// the LDS wait counter as well as the vector-memory one, so every wait for an
+// LDS read would also wait for all outstanding global stores.  Casting to the
+// global address space makes the compiler emit global_* instructions.
+#define MUON_GLOBAL __attribute__((address_space(1)))
+template <int BYTES> struct GWord;
+template <> struct GWord<2> { using T = uint16_t; };
+template <> struct GWord<4> { using T = uint32_t; };
+template <> struct GWord<8> { using T = uint32_t __attribute__((ext_vector_type(2))); };
+template <> struct GWord<16> { using T = uint32_t __attribute__((ext_vector_type(4))); };
+template <class T>
+__device__ __forceinline__ T gld(const T* p) {
+    using W = typename GWord<sizeof(T)>::T;
+    return __builtin_bit_cast(T, *(const MUON_GLOBAL W*)p);
+}
+template <class T>
+__device__ __forceinline__ void gst(T* p, const T& v) {
+    using W = typename GWord<sizeof(T)>::T;
+    *(MUON_GLOBAL W*)p = __builtin_bit_cast(W, v);
+}
+
 // Canonical Newton-Schulz buffers are padded to these multiples so the GEMM
 // kernels run on whole tiles with no bounds checks.  The padding is zero and
 // the iteration keeps it zero: rows/cols of zeros stay zero under X X^T,
@@ -66,7 +89,7 @@ __device__ __forceinline__ int find_matrix(const int32_t* prefix, int n, int32_t
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
-        if (__builtin_nontemporal_load(prefix + mid) <= tile) lo = mid; else hi = mid - 1;
+        if (gld(prefix + mid) <= tile) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
