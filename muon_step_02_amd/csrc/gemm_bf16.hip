@@ -127,24 +127,44 @@ struct Epi {
     float post;
 };
 
+// Fragments of MFMA k-step kk (16 deep) of one LDS slab: FM row blocks of
+// the P operand and FN of the Q operand for this wave.
 template <class C>
-__device__ __forceinline__ void mfma_stage(const uint16_t* sp, f32x16 (&acc)[C::FM][C::FN], int wm,
-                                           int wn, int frow, int khalf) {
+struct Frags {
+    bf16x8 a[C::FM], b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(const uint16_t* sp, int kk, int wm, int wn, int frow,
+                                           int khalf, Frags<C>& f) {
     const uint16_t* sq = sp + C::BM * C::BK;
+    const int lch = 2 * kk + khalf;
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-        const int lch = 2 * kk + khalf;
-        bf16x8 a[C::FM], b[C::FN];
+    for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
+    for (int j = 0; j < C::FN; ++j) f.b[j] = read_frag<C>(sq, wn * C::TN + j * 32 + frow, lch);
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_frags(f32x16 (&acc)[C::FM][C::FN], const Frags<C>& f) {
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) b[j] = read_frag<C>(sq, wn * C::TN + j * 32 + frow, lch);
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling pattern for one k-step: alternate NR LDS reads (the next
+// k-step's fragments) with the MFMAs of this one, so the reads are issued
+// early and their latency hides under the matrix work.
+template <int NR, int NM>
+__device__ __forceinline__ void interleave_reads_mfma() {
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int t = 0; t < NR && t < NM; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
+    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
 }
 
 template <int N>
@@ -164,6 +184,19 @@ struct Stages {
 template <class C>
 __device__ __forceinline__ uint16_t* stage(const Stages& st, int i) {
     return i == 0 ? st.s[0] : i == 1 ? st.s[1] : i == 2 ? st.s[2] : st.s[3];
+}
+
+// E chunks of one epilogue band, in the order the combine pass reads them.
+template <class C, int QN>
+__device__ __forceinline__ void load_e_band(const Epi& ep, int64_t row0, int64_t col0, int band,
+                                            uint4 (&e)[QN]) {
+    const int64_t brow = row0 + (int64_t)band * C::RB;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+        const int ch = q * C::NT + threadIdx.x;
+        const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
+        e[q] = gld(reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8));
+    }
 }
 
 // C tile = sum_k P[i][k] Q[j][k] for the BM rows starting at P0 and the BN
@@ -188,31 +221,56 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Software pipeline.  All NS stages are filled up front; while the
+    // MFMAs of k-step kk run, the fragments of k-step kk + 1 are read from
+    // LDS into the other register buffer.  The fragments of a slab's last
+    // k-step are read before the barrier that frees its stage and their
+    // MFMAs are issued after it, so the matrix cores have queued work while
+    // the waves meet.  The copy of slab kt + NS goes into the stage that slab
+    // kt leaves.
     const int KT = K / C::BK;
+    constexpr int KS = C::BK / 16;  // MFMA k-steps per slab (even)
 #pragma unroll
-    for (int u = 0; u < C::NS - 1; ++u) {
+    for (int u = 0; u < C::NS; ++u) {
         if (u < KT) {
             uint16_t* dst = stage<C>(st, u);
             load_slab<C, C::BM>(P0 + u * C::BK, ld, dst, wave, lane);
             load_slab<C, C::BN>(Q0 + u * C::BK, ld, dst + C::BM * C::BK, wave, lane);
         }
     }
+    if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * C::LPS>(); else wait_vmcnt<0>();
+    __syncthreads();
+    Frags<C> f[2];
+    read_frags<C>(stage<C>(st, 0), 0, wm, wn, frow, khalf, f[0]);
+
     for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
 #pragma unroll
         for (int u = 0; u < C::NS; ++u) {
             const int kt = kt0 + u;
             if (kt < KT) {
-                // this wave's copies of slab kt have landed once at most the
-                // later slabs' copies are outstanding; then every wave's
-                if (kt + C::NS - 2 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
-                __syncthreads();
-                if (kt + C::NS - 1 < KT) {
-                    uint16_t* dst = stage<C>(st, (u + C::NS - 1) % C::NS);
-                    const int64_t k0 = (int64_t)(kt + C::NS - 1) * C::BK;
-                    load_slab<C, C::BM>(P0 + k0, ld, dst, wave, lane);
-                    load_slab<C, C::BN>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    if (kk + 1 < KS) {
+                        read_frags<C>(stage<C>(st, u), kk + 1, wm, wn, frow, khalf, f[(kk + 1) & 1]);
+                    } else {
+                        // slab kt + 1 has landed once only the copies of the
+                        // slabs after it are outstanding; then every wave's.
+                        // The last slab takes the same path (its reads of
+                        // the next stage are unused) so every slab has one
+                        // straight-line sequence of LDS waits.
+                        if (kt + C::NS - 1 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
+                        __syncthreads();
+                        if (kt + C::NS < KT) {
+                            uint16_t* dst = stage<C>(st, u);
+                            const int64_t k0 = (int64_t)(kt + C::NS) * C::BK;
+                            load_slab<C, C::BM>(P0 + k0, ld, dst, wave, lane);
+                            load_slab<C, C::BN>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
+                        }
+                        read_frags<C>(stage<C>(st, (u + 1) % C::NS), 0, wm, wn, frow, khalf, f[0]);
+                    }
+                    mfma_frags<C>(acc, f[kk & 1]);
+                    interleave_reads_mfma<C::FM + C::FN, C::FM * C::FN>();
                 }
-                mfma_stage<C>(stage<C>(st, u), acc, wm, wn, frow, khalf);
             }
         }
     }
@@ -222,9 +280,18 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
     // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
     // combines 8 consecutive columns with E and stores 16 bytes of the output,
     // and, for the transposed copy, 8 consecutive rows of one column.
+    //
+    // The band loop is unrolled so the compiler can count outstanding memory
+    // operations exactly: no wait ever covers the stores of earlier bands, and
+    // E is loaded one band ahead so its latency hides behind the LDS work.
     float* sb = reinterpret_cast<float*>(st.s[0]);
-#pragma unroll 1
+    constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
+    uint4 ecur[QN], enxt[QN];
+    wait_vmcnt<0>();  // every slab copy has landed: the band buffer is free
+    if (HAS_E) load_e_band<C, QN>(ep, row0, col0, 0, ecur);
+#pragma unroll
     for (int band = 0; band < C::BM / C::RB; ++band) {
+        if (HAS_E && band + 1 < C::BM / C::RB) load_e_band<C, QN>(ep, row0, col0, band + 1, enxt);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
@@ -270,8 +337,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
             const float4 a1 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8 + 4);
             float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             if (HAS_E) {
-                const uint4 ev = gld(reinterpret_cast<const uint4*>(ep.E + (brow + rr) * ep.ld_e + col0 + c8));
-                const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w};
+                const uint32_t ew[4] = {ecur[q].x, ecur[q].y, ecur[q].z, ecur[q].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t w = ew[e >> 1];
@@ -309,6 +375,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
                 o.w = pack2(v[6], v[7]);
                 gst(reinterpret_cast<uint4*>(ep.outT + (col0 + c) * ep.ld_outT + brow + i8), o);
             }
+        }
+        if (HAS_E) {
+#pragma unroll
+            for (int q = 0; q < QN; ++q) ecur[q] = enxt[q];
         }
     }
 }
