@@ -238,16 +238,15 @@ const char* muon_status_str(muon_status s);
  * input.
  *   gram:   A = s2 * X X^T          (X: m x n, A: m x m)
  *   poly:   B = b*A + c*A A         (A, B: m x m, A symmetric)
- *   update: Xo = s*(a*X + B X), XoT = Xo^T  (X: m x n; XoT: n x m)
+ *   update: Xo = s*(a*X + B X)       (X, Xo: m x n, ld ldx; B: m x m, ld ldb)
  */
 muon_status muon_test_gram_bf16(muon_handle h, const void* X, void* A, int64_t m,
                                 int64_t n, int64_t ldx, int64_t lda, float s2, void* stream);
 muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m,
                                 int64_t lda, float b, float c, void* stream);
-muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* XT,
-                                  const void* B, void* Xo, void* XoT, int64_t m,
-                                  int64_t n, int64_t ldx, int64_t ldb, float a,
-                                  float s, void* stream);
+muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B,
+                                  void* Xo, int64_t m, int64_t n, int64_t ldx,
+                                  int64_t ldb, float a, float s, void* stream);
 
 #ifdef __cplusplus
 }

@@ -132,7 +132,7 @@ def load():
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_test_gram_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, vp]
     lib.muon_test_poly_bf16.argtypes = [vp, vp, vp, i64, i64, f32, f32, vp]
-    lib.muon_test_update_bf16.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
+    lib.muon_test_update_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
     lib.adamw_workspace_size.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.adamw_step_clipped.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
@@ -326,10 +326,9 @@ def muon_test_poly_bf16(h, A, B, m, lda, b, c, stream=None):
                                       _stream_ptr(stream)), "muon_test_poly_bf16")
 
 
-def muon_test_update_bf16(h, X, XT, B, Xo, XoT, m, n, ldx, ldb, a, s=1.0, stream=None):
-    _check(load().muon_test_update_bf16(h, X.data_ptr(), XT.data_ptr(), B.data_ptr(),
-                                        Xo.data_ptr(), XoT.data_ptr(), m, n, ldx, ldb, a, s,
-                                        _stream_ptr(stream)), "muon_test_update_bf16")
+def muon_test_update_bf16(h, X, B, Xo, m, n, ldx, ldb, a, s=1.0, stream=None):
+    _check(load().muon_test_update_bf16(h, X.data_ptr(), B.data_ptr(), Xo.data_ptr(), m, n, ldx,
+                                        ldb, a, s, _stream_ptr(stream)), "muon_test_update_bf16")
 
 
 def muon_profile_enable(h, enable=True):

@@ -293,9 +293,13 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         MatDesc& d = P.d[k];
         const size_t xb = (size_t)d.mp * (size_t)d.np * es;
         const size_t ab = (size_t)d.mp * (size_t)d.mp * es;
+        // X^T is kept only by the fp32 iteration; the bf16 update reads X
+        // k-major directly
+        d.xt[0] = d.xt[1] = nullptr;
         void** bufs[4] = {&d.x[0], &d.x[1], &d.xt[0], &d.xt[1]};
-        for (void** b : bufs) {
-            *b = reinterpret_cast<void*>(ws + off);
+        const int nbufs = P.ns_f32 ? 4 : 2;
+        for (int i = 0; i < nbufs; ++i) {
+            *bufs[i] = reinterpret_cast<void*>(ws + off);
             off = align_up(off + xb, 256);
         }
         d.a = reinterpret_cast<void*>(ws + off);
@@ -700,15 +704,14 @@ muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
-muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* XT, const void* B,
-                                  void* Xo, void* XoT, int64_t m, int64_t n, int64_t ldx,
-                                  int64_t ldb, float a, float s, void* stream) {
+muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B, void* Xo,
+                                  int64_t m, int64_t n, int64_t ldx, int64_t ldb, float a, float s,
+                                  void* stream) {
     muon_status st = check_single(h, m, n);
     if (st != MUON_OK) return st;
-    if (!X || !XT || !B || !Xo || !XoT || ldx < n || ldb < m || ldx % 8 || ldb % 8)
-        return MUON_ERR_INVALID_ARG;
+    if (!X || !B || !Xo || ldx < n || ldb < m || ldx % 8 || ldb % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    return hip_status(launch_update_bf16_single(X, XT, B, Xo, XoT, (int)m, (int)n, ldx, ldb, a, s,
+    return hip_status(launch_update_bf16_single(X, B, Xo, (int)m, (int)n, ldx, ldb, a, s,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -158,9 +158,13 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     const int64_t rows = d.rows, cols = d.cols;
     const int gbf = d.grad_dtype == MUON_BF16;
     // natural orientation (rows_pad x cols_pad, ld cols_pad) and transposed
-    // orientation (cols_pad x rows_pad, ld rows_pad) of Y
+    // orientation (cols_pad x rows_pad, ld rows_pad) of Y.  The fp32
+    // iteration keeps both X and X^T; the bf16 one only the canonical X
+    // (short side first), which is Y itself or Y^T.
     void* nat = d.transposed ? d.xt[0] : d.x[0];
     void* trn = d.transposed ? d.x[0] : d.xt[0];
+    const bool write_nat = NS_F32 || !d.transposed;
+    const bool write_trn = NS_F32 || d.transposed;
     const int64_t ld_nat = d.cols_pad, ld_trn = d.rows_pad;
     const float omm = 1.f - mu;
     float ss = 0.f;
@@ -194,18 +198,20 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
             }
             store4<VEC>(d.mom, 0, r * d.ld_mom + c, m[q], valid[q]);
         }
-        store_ns4<NS_F32>(nat, r * ld_nat + c, y);
+        if (write_nat) store_ns4<NS_F32>(nat, r * ld_nat + c, y);
 #pragma unroll
         for (int e = 0; e < 4; ++e) tileT[cg + e][lr] = y[e];
     }
-    __syncthreads();
+    if (write_trn) {
+        __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int lc = rr + 16 * q;  // column of the weight = row of Y^T
-        float v[4];
+        for (int q = 0; q < 4; ++q) {
+            const int lc = rr + 16 * q;  // column of the weight = row of Y^T
+            float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = tileT[lc][cg + e];
-        store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cg, v);
+            for (int e = 0; e < 4; ++e) v[e] = tileT[lc][cg + e];
+            store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cg, v);
+        }
     }
     const float tot = block_sum_256(ss, red);
     if (threadIdx.x == 0) gst(d.partials + lt, tot);
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
 
 template <bool VEC, bool NS_F32>
 __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity, float decay,
-                                           float step, float qk_tau) {
+                                           float step, float qk_tau, float (*tileT)[kEwTile + 1]) {
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
     const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
     const int t = threadIdx.x;
@@ -256,21 +262,41 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
     const int rr = t >> 4;
     const int64_t rows = d.rows, cols = d.cols;
     const int pbf = d.param_dtype == MUON_BF16;
-    // O in the weight's orientation: X when not transposed, X^T otherwise;
-    // either way rows_pad x cols_pad with ld cols_pad.
-    const void* O = d.transposed ? d.xt[parity] : d.x[parity];
+    // O in the weight's orientation (rows_pad x cols_pad, ld cols_pad): X
+    // when not transposed, else X^T, which the fp32 iteration keeps and the
+    // bf16 one gets by transposing X (cols_pad x rows_pad) through LDS.
+    const bool via_lds = !NS_F32 && d.transposed;
+    const void* O = d.transposed ? (NS_F32 ? d.xt[parity] : d.x[parity]) : d.x[parity];
     const int64_t ld_o = d.cols_pad;
     const float sc = step * d.scale;
     float o[4][4];
     Vals4 w[4];
     int valid[4];
+    if (via_lds) {
+        // X rows c0.. (weight columns), columns r0.. (weight rows); all inside
+        // the zero-padded buffer
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int lc = rr + 16 * q;
+            float v[4];
+            load_ns4<NS_F32>(O, (c0 + lc) * d.rows_pad + r0 + cg, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tileT[lc][cg + e] = v[e];
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int64_t r = r0 + rr + 16 * q;
         const int64_t cv = cols - (c0 + cg);
         valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
         if (valid[q] > 0) {
-            load_ns4<NS_F32>(O, r * ld_o + c0 + cg, o[q]);
+            if (via_lds) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[q][e] = tileT[cg + e][rr + 16 * q];
+            } else {
+                load_ns4<NS_F32>(O, r * ld_o + c0 + cg, o[q]);
+            }
             w[q] = load4<VEC>(d.param, pbf, r * d.ld_param + c0 + cg, valid[q]);
         }
     }
@@ -302,14 +328,15 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
                                                     const int32_t* __restrict__ prefix,
                                                     int parity, float decay, float step,
                                                     float qk_tau) {
+    __shared__ float tileT[NS_F32 ? 1 : kEwTile][kEwTile + 1];
     const int tile = blockIdx.x;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
     if (d.vec4)
-        apply_tile<true, NS_F32>(d, lt, parity, decay, step, qk_tau);
+        apply_tile<true, NS_F32>(d, lt, parity, decay, step, qk_tau, tileT);
     else
-        apply_tile<false, NS_F32>(d, lt, parity, decay, step, qk_tau);
+        apply_tile<false, NS_F32>(d, lt, parity, decay, step, qk_tau, tileT);
 }
 
 // ---------------------------------------------------------------- AdamW ----

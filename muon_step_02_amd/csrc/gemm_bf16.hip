@@ -10,13 +10,12 @@
 //   poly:   B = b A + c A A              m' x m', symmetric (A A = A A^T)
 //   update: X <- a X + B X               m' x n'
 //
-// All three are "NT" products C[i][j] = sum_k P[i][k] Q[j][k] with both
-// operands read along contiguous rows: X's rows for the Gram, A's rows for
-// the polynomial (A is symmetric), and for the update B's rows and the rows
-// of X^T, which the update itself writes next to X (and the momentum kernel
-// before the first iteration).  Keeping X^T costs one extra bf16 store per
-// element per iteration and turns every operand load into a direct
-// global->LDS copy.
+// The Gram and the polynomial are "NT" products C[i][j] = sum_k P[i][k] Q[j][k]
+// with both operands read along contiguous rows (X's rows; A's rows, A being
+// symmetric).  The update C[i][j] = sum_k B[i][k] X[k][j] reads B by rows and
+// X in its natural k-major layout: slabs of X rows are copied to LDS as they
+// are and the MFMA operand is gathered with the transposing LDS read
+// (ds_read_b64_tr_b16), so no transposed copy of X is ever stored.
 //
 // The Gram and the polynomial outputs are symmetric: only tiles on or below
 // the diagonal are computed and each off-diagonal tile is stored twice (as
@@ -40,6 +39,7 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -109,6 +109,55 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* slab, int row, int l
     return *reinterpret_cast<const bf16x8*>(slab + row * C::BK + pch * 8);
 }
 
+// k-major operand (the update's X): an LDS slab holds BK rows k of BN
+// columns, 2 BN bytes per row, the 16-byte chunk c of row k at position
+// c ^ swzk(k).  A transposing read by 16 lanes covers 4 consecutive rows x
+// 64 bytes; swzk spreads those 4 rows over disjoint quarters of the 256-byte
+// bank space.
+__device__ __forceinline__ int swzk(int k) { return (k & 3) << 2; }
+
+// Copy rows [0, BK) (k) x columns [0, BN) of a row-major bf16 matrix (row k
+// at g + k * ld) into a k-major slab.  One global_load_lds_dwordx4 moves 1 KB
+// = 1024 / (2 BN) rows; lane L fills chunk position L % CQ of row L / CQ.
+template <class C>
+__device__ __forceinline__ void load_slab_kn(const uint16_t* __restrict__ g, int64_t ld,
+                                             uint16_t* slab, int wave, int lane) {
+    constexpr int CQ = C::BN / 8;          // 16-byte chunks per row
+    constexpr int RPK = 64 / CQ;           // rows per copy
+    constexpr int PER_WAVE = (C::BK / RPK) / C::NW;
+    static_assert((C::BK / RPK) % C::NW == 0, "k-major slab rows must split over waves");
+    const int lrow = lane / CQ;
+    const int p = lane % CQ;
+#pragma unroll
+    for (int q = 0; q < PER_WAVE; ++q) {
+        const int grp = wave * PER_WAVE + q;
+        const int k = grp * RPK + lrow;
+        const uint16_t* src = g + (int64_t)k * ld + (p ^ swzk(k)) * 8;
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * RPK * C::BN),
+                                         16, 0, 0);
+    }
+}
+
+// MFMA B-operand fragment (lane l: column n0 + l % 32, k = k0 + 8 (l / 32) +
+// 0..7) from a k-major slab, as two transposing 8-byte reads.  In each group
+// of 16 lanes, lane a + 4 b addresses row b, columns 4a..4a+3 of a 4 x 16
+// block and receives column (lane % 16) of rows 0..3.
+template <class C>
+__device__ __forceinline__ bf16x8 read_frag_kn(const uint16_t* slab, int k0, int n0, int lane) {
+    const int g = lane >> 4, s16 = lane & 15;
+    const int a = s16 & 3, b = s16 >> 2;
+    const int n = n0 + 16 * (g & 1) + 4 * a;
+    i16x4 h[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int k = k0 + 8 * (g >> 1) + 4 * t + b;
+        const uint16_t* p = slab + k * C::BN + (((n >> 3) ^ swzk(k)) << 3) + (n & 7);
+        h[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
@@ -127,6 +176,19 @@ struct Epi {
     float post;
 };
 
+// Copy the operand slabs of k-range [k0, k0 + BK) into one LDS stage: the
+// BM x BK slab of P, then Q's (BN x BK, or BK x BN k-major).
+template <class C, bool QKN>
+__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ P0, int64_t ldp,
+                                           const uint16_t* __restrict__ Q0, int64_t ldq,
+                                           int64_t k0, uint16_t* dst, int wave, int lane) {
+    load_slab<C, C::BM>(P0 + k0, ldp, dst, wave, lane);
+    if (QKN)
+        load_slab_kn<C>(Q0 + k0 * ldq, ldq, dst + C::BM * C::BK, wave, lane);
+    else
+        load_slab<C, C::BN>(Q0 + k0, ldq, dst + C::BM * C::BK, wave, lane);
+}
+
 // Fragments of MFMA k-step kk (16 deep) of one LDS slab: FM row blocks of
 // the P operand and FN of the Q operand for this wave.
 template <class C>
@@ -134,15 +196,17 @@ struct Frags {
     bf16x8 a[C::FM], b[C::FN];
 };
 
-template <class C>
+template <class C, bool QKN>
 __device__ __forceinline__ void read_frags(const uint16_t* sp, int kk, int wm, int wn, int frow,
-                                           int khalf, Frags<C>& f) {
+                                           int khalf, int lane, Frags<C>& f) {
     const uint16_t* sq = sp + C::BM * C::BK;
     const int lch = 2 * kk + khalf;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j) f.b[j] = read_frag<C>(sq, wn * C::TN + j * 32 + frow, lch);
+    for (int j = 0; j < C::FN; ++j)
+        f.b[j] = QKN ? read_frag_kn<C>(sq, 16 * kk, wn * C::TN + j * 32, lane)
+                     : read_frag<C>(sq, wn * C::TN + j * 32 + frow, lch);
 }
 
 template <class C>
@@ -154,17 +218,20 @@ __device__ __forceinline__ void mfma_frags(f32x16 (&acc)[C::FM][C::FN], const Fr
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling pattern for one k-step: alternate NR LDS reads (the next
-// k-step's fragments) with the MFMAs of this one, so the reads are issued
-// early and their latency hides under the matrix work.
-template <int NR, int NM>
+// Scheduling pattern for one k-step: the NR LDS reads of the next k-step's
+// fragments go out RPM at a time between this k-step's NM MFMAs, so they are
+// issued early and their latency hides under the matrix work.
+template <int NR, int NM, int RPM, int T = 0>
 __device__ __forceinline__ void interleave_reads_mfma() {
-#pragma unroll
-    for (int t = 0; t < NR && t < NM; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    constexpr int G = (NR + RPM - 1) / RPM;  // MFMAs that carry reads
+    if constexpr (T < G && T < NM) {
+        constexpr int nr = (T + 1) * RPM <= NR ? RPM : NR - T * RPM;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // DS read
+        interleave_reads_mfma<NR, NM, RPM, T + 1>();
+    } else if constexpr (NM > T) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - T, 0);
     }
-    if (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
 }
 
 template <int N>
@@ -199,14 +266,15 @@ __device__ __forceinline__ void load_e_band(const Epi& ep, int64_t row0, int64_t
     }
 }
 
-// C tile = sum_k P[i][k] Q[j][k] for the BM rows starting at P0 and the BN
-// rows starting at Q0 (both leading dimension ld, K a multiple of BK), then
-// the epilogue.  NS-stage pipeline: the copy of slab k + NS - 1 is issued
-// while the MFMAs run on slab k.
-template <class C, bool HAS_E>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const uint16_t* __restrict__ Q0,
-                                          int64_t ld, int K, int64_t row0, int64_t col0,
-                                          const Epi& ep, const Stages& st) {
+// C tile = sum_k P[i][k] Q'[k][j] for the BM rows starting at P0 (leading
+// dimension ldp) and BN columns of Q' (K a multiple of BK), then the
+// epilogue.  Q' is read as Q'[k][j] = Q0[j * ldq + k] (NT) or, with QKN, as
+// Q0[k * ldq + j] (k-major).
+template <class C, bool HAS_E, bool QKN = false>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64_t ldp,
+                                          const uint16_t* __restrict__ Q0, int64_t ldq, int K,
+                                          int64_t row0, int64_t col0, const Epi& ep,
+                                          const Stages& st) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -233,15 +301,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
 #pragma unroll
     for (int u = 0; u < C::NS; ++u) {
         if (u < KT) {
-            uint16_t* dst = stage<C>(st, u);
-            load_slab<C, C::BM>(P0 + u * C::BK, ld, dst, wave, lane);
-            load_slab<C, C::BN>(Q0 + u * C::BK, ld, dst + C::BM * C::BK, wave, lane);
+            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, stage<C>(st, u), wave, lane);
         }
     }
     if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * C::LPS>(); else wait_vmcnt<0>();
     __syncthreads();
     Frags<C> f[2];
-    read_frags<C>(stage<C>(st, 0), 0, wm, wn, frow, khalf, f[0]);
+    read_frags<C, QKN>(stage<C>(st, 0), 0, wm, wn, frow, khalf, lane, f[0]);
 
     for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
 #pragma unroll
@@ -251,7 +317,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     if (kk + 1 < KS) {
-                        read_frags<C>(stage<C>(st, u), kk + 1, wm, wn, frow, khalf, f[(kk + 1) & 1]);
+                        read_frags<C, QKN>(stage<C>(st, u), kk + 1, wm, wn, frow, khalf, lane,
+                                           f[(kk + 1) & 1]);
                     } else {
                         // slab kt + 1 has landed once only the copies of the
                         // slabs after it are outstanding; then every wave's.
@@ -261,15 +328,15 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, const
                         if (kt + C::NS - 1 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
                         __syncthreads();
                         if (kt + C::NS < KT) {
-                            uint16_t* dst = stage<C>(st, u);
-                            const int64_t k0 = (int64_t)(kt + C::NS) * C::BK;
-                            load_slab<C, C::BM>(P0 + k0, ld, dst, wave, lane);
-                            load_slab<C, C::BN>(Q0 + k0, ld, dst + C::BM * C::BK, wave, lane);
+                            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)(kt + C::NS) * C::BK,
+                                               stage<C>(st, u), wave, lane);
                         }
-                        read_frags<C>(stage<C>(st, (u + 1) % C::NS), 0, wm, wn, frow, khalf, f[0]);
+                        read_frags<C, QKN>(stage<C>(st, (u + 1) % C::NS), 0, wm, wn, frow, khalf,
+                                           lane, f[0]);
                     }
                     mfma_frags<C>(acc, f[kk & 1]);
-                    interleave_reads_mfma<C::FM + C::FN, C::FM * C::FN>();
+                    // the k-major reads are twice as many: front-load them
+                    interleave_reads_mfma<C::FM + (QKN ? 2 : 1) * C::FN, C::FM * C::FN, QKN ? 2 : 1>();
                 }
             }
         }
@@ -454,7 +521,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
 }
 
 template <class C>
@@ -475,19 +542,19 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     int ti, tj;
     grouped_index(lt, (int)(mp / C::BM), (int)(np / C::BN), ti, tj);
     const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
-    const uint16_t* XT = reinterpret_cast<const uint16_t*>(d.xt[it & 1]);
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
     Epi ep;
     ep.out = reinterpret_cast<uint16_t*>(d.x[(it + 1) & 1]);
     ep.ld_out = np;
-    ep.outT = reinterpret_cast<uint16_t*>(d.xt[(it + 1) & 1]);
-    ep.ld_outT = mp;
-    ep.E = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = X;
     ep.ld_e = np;
     ep.coef_e = ca;
     ep.coef_acc = 1.f;
     ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * mp, XT + c0 * mp, mp, (int)mp, r0, c0, ep, st);
+    gemm_tile<C, true, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
 }
 
 // single-matrix variants for the test hooks
@@ -515,16 +582,15 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
         ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
 }
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __restrict__ X,
-                                                          const uint16_t* __restrict__ XT,
                                                           const uint16_t* __restrict__ B,
-                                                          uint16_t* Xo, uint16_t* XoT, int m,
-                                                          int n, int64_t ldx, int64_t ldb, float ca,
-                                                          float s, XcdSplit xs) {
+                                                          uint16_t* Xo, int m, int n, int64_t ldx,
+                                                          int64_t ldb, float ca, float s,
+                                                          XcdSplit xs) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
@@ -535,10 +601,10 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     int ti, tj;
     grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
     Epi ep;
-    ep.out = Xo; ep.ld_out = ldx; ep.outT = XoT; ep.ld_outT = ldb;
+    ep.out = Xo; ep.ld_out = ldx; ep.outT = nullptr; ep.ld_outT = 0;
     ep.E = X; ep.ld_e = ldx; ep.coef_e = ca; ep.coef_acc = 1.f; ep.post = s;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true>(B + r0 * ldb, XT + c0 * ldb, ldb, m, r0, c0, ep, st);
+    gemm_tile<C, true, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
 }
 
 inline int xcd_grid(const XcdSplit& xs) { return 8 * (xs.per > 0 ? xs.per : 1); }
@@ -639,17 +705,15 @@ hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, f
     return hipGetLastError();
 }
 
-hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* B, void* Xo,
-                                     void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
-                                     float s, hipStream_t st) {
+hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
+                                     int64_t ldx, int64_t ldb, float a, float s, hipStream_t st) {
     const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
     const int32_t total = tiles;
     const int64_t w = 1;
     const XcdSplit xs = xcd_split(&total, &w, 1);
     ns_update_single<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(
-        reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(XT),
-        reinterpret_cast<const uint16_t*>(B), reinterpret_cast<uint16_t*>(Xo),
-        reinterpret_cast<uint16_t*>(XoT), m, n, ldx, ldb, a, s, xs);
+        reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
+        reinterpret_cast<uint16_t*>(Xo), m, n, ldx, ldb, a, s, xs);
     return hipGetLastError();
 }
 

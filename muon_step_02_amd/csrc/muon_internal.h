@@ -69,7 +69,7 @@ struct MatDesc {
     float scale;         // shape multiplier * extra_scale
     // workspace buffers (bf16 or f32 elements by ns dtype)
     void* x[2];   // canonical X, mp x np, ld np (ping-pong)
-    void* xt[2];  // X^T, np x mp, ld mp (ping-pong)
+    void* xt[2];  // X^T, np x mp, ld mp (ping-pong; fp32 iteration only, else null)
     void* a;      // A = X X^T, mp x mp
     void* b;      // B = b A + c A A, mp x mp
     float* partials;  // one sum of squares per elementwise tile
@@ -156,9 +156,8 @@ hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t
                                    float s2, hipStream_t st);
 hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
                                    hipStream_t st);
-hipError_t launch_update_bf16_single(const void* X, const void* XT, const void* B, void* Xo,
-                                     void* XoT, int m, int n, int64_t ldx, int64_t ldb, float a,
-                                     float s, hipStream_t st);
+hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
+                                     int64_t ldx, int64_t ldb, float a, float s, hipStream_t st);
 
 // AdamW: tensors travel in kernel arguments, kAdamwGroup per launch.
 constexpr int kAdamwGroup = 32;

@@ -63,24 +63,26 @@ def test_poly_phase(m):
     assert np.array_equal(got, got.T)
 
 
-@pytest.mark.parametrize("m,n", [(256, 256), (256, 768), (512, 1024)])
+@pytest.mark.parametrize("m,n,ldx", [(256, 256, 256), (256, 768, 768), (512, 1024, 1024),
+                                      (256, 512, 768)])
 @pytest.mark.parametrize("s", [1.0, 0.5])
-def test_update_phase(m, n, s):
+def test_update_phase(m, n, ldx, s):
+    # X is read k-major (rows of X are the update's k); ldx > n checks that
+    # the columns beyond n are neither read into the product nor written
     h = Handle.get()
-    X = _bf16((m, n), 3 + m, 1.0 / np.sqrt(n))
-    XT = X.T.contiguous()
+    Xfull = _bf16((m, ldx), 3 + m, 1.0 / np.sqrt(n))
+    X = Xfull[:, :n]
     B = _sym_bf16(m, 5 + n, 1.0 / np.sqrt(m))
-    Xo = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device=DEV)
-    XoT = torch.full((n, m), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Xo = torch.full((m, ldx), float("nan"), dtype=torch.bfloat16, device=DEV)
     a = 3.4445
-    mu.muon_test_update_bf16(h, X, XT, B, Xo, XoT, m, n, n, m, a, s)
+    mu.muon_test_update_bf16(h, Xfull, B, Xo, m, n, ldx, m, a, s)
     torch.cuda.synchronize()
     X64, B64 = f64(X), f64(B)
     want = s * (a * X64 + B64 @ X64)
-    got = f64(Xo)
+    got = f64(Xo[:, :n])
     assert np.isfinite(got).all()
     assert relF(got, want) < 4e-3
-    assert np.array_equal(f64(XoT), got.T)
+    assert np.isnan(f64(Xo[:, n:])).all()
 
 
 # ------------------------------------------------------------ whole steps --
