@@ -237,16 +237,18 @@ const char* muon_status_str(muon_status s);
  * tests can compare each GEMM against the oracle's intermediate on the same
  * input.
  *   gram:   A = s2 * X X^T          (X: m x n, A: m x m)
- *   poly:   B = b*A + c*A A         (A, B: m x m, A symmetric)
- *   update: Xo = s*(a*X + B X)       (X, Xo: m x n, ld ldx; B: m x m, ld ldb)
+ *   poly:   B = a*I + b*A + c*A A   (A, B: m x m, A symmetric)
+ *   update: Xo = s * B X             (X, Xo: m x n, ld ldx; B: m x m, ld ldb)
+ * (The quintic step a X + b A X + c A A X is (a I + b A + c A A) X: the
+ * identity term rides on B's diagonal and the update is a plain product.)
  */
 muon_status muon_test_gram_bf16(muon_handle h, const void* X, void* A, int64_t m,
                                 int64_t n, int64_t ldx, int64_t lda, float s2, void* stream);
 muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m,
-                                int64_t lda, float b, float c, void* stream);
+                                int64_t lda, float a, float b, float c, void* stream);
 muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B,
                                   void* Xo, int64_t m, int64_t n, int64_t ldx,
-                                  int64_t ldb, float a, float s, void* stream);
+                                  int64_t ldb, float s, void* stream);
 
 #ifdef __cplusplus
 }

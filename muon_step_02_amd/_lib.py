@@ -131,8 +131,8 @@ def load():
     lib.muon_status_str.argtypes = [i32]
     lib.muon_status_str.restype = ctypes.c_char_p
     lib.muon_test_gram_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, vp]
-    lib.muon_test_poly_bf16.argtypes = [vp, vp, vp, i64, i64, f32, f32, vp]
-    lib.muon_test_update_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, vp]
+    lib.muon_test_poly_bf16.argtypes = [vp, vp, vp, i64, i64, f32, f32, f32, vp]
+    lib.muon_test_update_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, f32, vp]
     lib.adamw_workspace_size.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.adamw_step_clipped.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
@@ -321,14 +321,16 @@ def muon_test_gram_bf16(h, X, A, m, n, ldx, lda, s2=1.0, stream=None):
                                       _stream_ptr(stream)), "muon_test_gram_bf16")
 
 
-def muon_test_poly_bf16(h, A, B, m, lda, b, c, stream=None):
-    _check(load().muon_test_poly_bf16(h, A.data_ptr(), B.data_ptr(), m, lda, b, c,
+def muon_test_poly_bf16(h, A, B, m, lda, a, b, c, stream=None):
+    """B = a I + b A + c A A (bf16, m x m, leading dimension lda)."""
+    _check(load().muon_test_poly_bf16(h, A.data_ptr(), B.data_ptr(), m, lda, a, b, c,
                                       _stream_ptr(stream)), "muon_test_poly_bf16")
 
 
-def muon_test_update_bf16(h, X, B, Xo, m, n, ldx, ldb, a, s=1.0, stream=None):
+def muon_test_update_bf16(h, X, B, Xo, m, n, ldx, ldb, s=1.0, stream=None):
+    """Xo = s B X (bf16; X, Xo m x n with leading dimension ldx, B m x m)."""
     _check(load().muon_test_update_bf16(h, X.data_ptr(), B.data_ptr(), Xo.data_ptr(), m, n, ldx,
-                                        ldb, a, s, _stream_ptr(stream)), "muon_test_update_bf16")
+                                        ldb, s, _stream_ptr(stream)), "muon_test_update_bf16")
 
 
 def muon_profile_enable(h, enable=True):

@@ -492,13 +492,13 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, b, c, k, s); });
+            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, a, b, c, k, s); });
         }
         for (int k = 0; k < 2 && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, a, k, s); });
+            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k, s); });
         }
     }
     if (e == hipSuccess)
@@ -695,23 +695,23 @@ muon_status muon_test_gram_bf16(muon_handle h, const void* X, void* A, int64_t m
 }
 
 muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m, int64_t lda,
-                                float b, float c, void* stream) {
+                                float a, float b, float c, void* stream) {
     muon_status st = check_single(h, m, m);
     if (st != MUON_OK) return st;
     if (!A || !B || lda < m || lda % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    return hip_status(launch_poly_bf16_single(A, B, (int)m, lda, b, c,
+    return hip_status(launch_poly_bf16_single(A, B, (int)m, lda, a, b, c,
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
 muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B, void* Xo,
-                                  int64_t m, int64_t n, int64_t ldx, int64_t ldb, float a, float s,
+                                  int64_t m, int64_t n, int64_t ldx, int64_t ldb, float s,
                                   void* stream) {
     muon_status st = check_single(h, m, n);
     if (st != MUON_OK) return st;
     if (!X || !B || !Xo || ldx < n || ldb < m || ldx % 8 || ldb % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    return hip_status(launch_update_bf16_single(X, B, Xo, (int)m, (int)n, ldx, ldb, a, s,
+    return hip_status(launch_update_bf16_single(X, B, Xo, (int)m, (int)n, ldx, ldb, s,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 

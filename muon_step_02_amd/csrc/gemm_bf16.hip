@@ -7,8 +7,11 @@
 // result):
 //
 //   gram:   A = X X^T                    m' x m', symmetric
-//   poly:   B = b A + c A A              m' x m', symmetric (A A = A A^T)
-//   update: X <- a X + B X               m' x n'
+//   poly:   B = a I + b A + c A A        m' x m', symmetric (A A = A A^T)
+//   update: X <- B X                     m' x n'
+//
+// (a X + (b A + c A A) X = B X with the identity term folded into B's
+// diagonal; the update then reads nothing but its two operands.)
 //
 // The Gram and the polynomial are "NT" products C[i][j] = sum_k P[i][k] Q[j][k]
 // with both operands read along contiguous rows (X's rows; A's rows, A being
@@ -168,12 +171,14 @@ struct Epi {
     int64_t ld_out;
     uint16_t* outT;
     int64_t ld_outT;
-    // v = post * (coef_acc * product + coef_e * E[i][j])   (E only if HAS_E)
+    // v = post * (coef_acc * product + coef_e * E[i][j]) + diag * [i == j]
+    // (E only if HAS_E; diag only on tiles that hold part of the diagonal)
     const uint16_t* E;
     int64_t ld_e;
     float coef_e;
     float coef_acc;
     float post;
+    float diag;
 };
 
 // Copy the operand slabs of k-range [k0, k0 + BK) into one LDS stage: the
@@ -415,6 +420,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = ep.post * (ep.coef_acc * v[e]);
             }
+            if (ep.diag != 0.f) {
+                const int64_t dc = brow + rr - (col0 + c8);  // column of the diagonal, relative
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += (dc == e) ? ep.diag : 0.f;
+            }
             uint4 o;
             o.x = pack2(v[0], v[1]);
             o.y = pack2(v[2], v[3]);
@@ -482,7 +492,8 @@ __device__ __forceinline__ void grouped_index(int lt, int trows, int tcols, int&
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict__ descs, int n,
                                                        const int32_t* __restrict__ prefix,
-                                                       XcdSplit xs, int it, float cb, float cc) {
+                                                       XcdSplit xs, int it, float ca, float cb,
+                                                       float cc) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
@@ -511,6 +522,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.coef_e = 0.f;
         ep.coef_acc = s * s;
         ep.post = 1.f;
+        ep.diag = 0.f;
     } else {
         src = reinterpret_cast<const uint16_t*>(d.a);
         ld = mp;
@@ -519,6 +531,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.coef_e = cb;
         ep.coef_acc = cc;
         ep.post = 1.f;
+        ep.diag = (ti == tj) ? ca : 0.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
     gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
 template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
                                                           const int32_t* __restrict__ prefix,
-                                                          XcdSplit xs, int it, float ca) {
+                                                          XcdSplit xs, int it) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
@@ -548,20 +561,22 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     ep.ld_out = np;
     ep.outT = nullptr;
     ep.ld_outT = 0;
-    ep.E = X;
-    ep.ld_e = np;
-    ep.coef_e = ca;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
     ep.coef_acc = 1.f;
     ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
+    ep.diag = 0.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
+    gemm_tile<C, false, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
 }
 
 // single-matrix variants for the test hooks
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
                                                        int K, uint16_t* out, int64_t ld_out,
-                                                       float sq, float cb, float cc, XcdSplit xs) {
+                                                       float sq, float ca, float cb, float cc,
+                                                       XcdSplit xs) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
@@ -578,8 +593,10 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
     ep.ld_outT = ld_out;
     if (PHASE == GRAM) {
         ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = sq; ep.post = 1.f;
+        ep.diag = 0.f;
     } else {
         ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
+        ep.diag = (ti == tj) ? ca : 0.f;
     }
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
     gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
@@ -589,8 +606,7 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __restrict__ X,
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* Xo, int m, int n, int64_t ldx,
-                                                          int64_t ldb, float ca, float s,
-                                                          XcdSplit xs) {
+                                                          int64_t ldb, float s, XcdSplit xs) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
@@ -602,9 +618,9 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
     Epi ep;
     ep.out = Xo; ep.ld_out = ldx; ep.outT = nullptr; ep.ld_outT = 0;
-    ep.E = X; ep.ld_e = ldx; ep.coef_e = ca; ep.coef_acc = 1.f; ep.post = s;
+    ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = 1.f; ep.post = s; ep.diag = 0.f;
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, true, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
+    gemm_tile<C, false, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
 }
 
 inline int xcd_grid(const XcdSplit& xs) { return 8 * (xs.per > 0 ? xs.per : 1); }
@@ -657,27 +673,27 @@ XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n) {
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st) {
     if (small)
-        ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f);
+        ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f, 0.f);
     else
-        ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f);
+        ns_sym_kernel<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f, 0.f);
     return hipGetLastError();
 }
 
-hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float b,
-                            float c, int small, hipStream_t st) {
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float a,
+                            float b, float c, int small, hipStream_t st) {
     if (small)
-        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, b, c);
+        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, a, b, c);
     else
-        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, b, c);
+        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, a, b, c);
     return hipGetLastError();
 }
 
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
-                              float a, int small, hipStream_t st) {
+                              int small, hipStream_t st) {
     if (small)
-        ns_update_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.upd, xs, it, a);
+        ns_update_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.upd, xs, it);
     else
-        ns_update_kernel<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(d, n, p.upd, xs, it, a);
+        ns_update_kernel<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(d, n, p.upd, xs, it);
     return hipGetLastError();
 }
 
@@ -689,31 +705,31 @@ hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t
     const XcdSplit xs = xcd_split(&total, &w, 1);
     ns_sym_single<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), ldx, n, reinterpret_cast<uint16_t*>(A), lda, s2, 0.f,
-        0.f, xs);
+        0.f, 0.f, xs);
     return hipGetLastError();
 }
 
-hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
-                                   hipStream_t st) {
+hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float a, float b,
+                                   float c, hipStream_t st) {
     const int T = m / SymCfg::BM;
     const int32_t total = T * (T + 1) / 2;
     const int64_t w = 1;
     const XcdSplit xs = xcd_split(&total, &w, 1);
     ns_sym_single<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
-        reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, b,
-        c, xs);
+        reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, a,
+        b, c, xs);
     return hipGetLastError();
 }
 
 hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
-                                     int64_t ldx, int64_t ldb, float a, float s, hipStream_t st) {
+                                     int64_t ldx, int64_t ldb, float s, hipStream_t st) {
     const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
     const int32_t total = tiles;
     const int64_t w = 1;
     const XcdSplit xs = xcd_split(&total, &w, 1);
     ns_update_single<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
-        reinterpret_cast<uint16_t*>(Xo), m, n, ldx, ldb, a, s, xs);
+        reinterpret_cast<uint16_t*>(Xo), m, n, ldx, ldb, s, xs);
     return hipGetLastError();
 }
 

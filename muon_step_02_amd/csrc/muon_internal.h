@@ -136,10 +136,11 @@ XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n);
 
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st);
-hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float b,
-                            float c, int small, hipStream_t st);
+// poly writes B = a I + b A + c A A, so the update is the plain product B X
+hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float a,
+                            float b, float c, int small, hipStream_t st);
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
-                              float a, int small, hipStream_t st);
+                              int small, hipStream_t st);
 int gemm_tile_bf16(int small);  // square tile edge of the Gram/polynomial kernels
 int upd_tile_m_bf16(int small);
 int upd_tile_n_bf16(int small);
@@ -154,10 +155,10 @@ constexpr int kTileF32 = 64;
 // single-phase test hooks (one matrix, caller buffers)
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
                                    float s2, hipStream_t st);
-hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float b, float c,
-                                   hipStream_t st);
+hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float a, float b,
+                                   float c, hipStream_t st);
 hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
-                                     int64_t ldx, int64_t ldb, float a, float s, hipStream_t st);
+                                     int64_t ldx, int64_t ldb, float s, hipStream_t st);
 
 // AdamW: tensors travel in kernel arguments, kAdamwGroup per launch.
 constexpr int kAdamwGroup = 32;

@@ -52,14 +52,18 @@ def test_poly_phase(m):
     h = Handle.get()
     A = _sym_bf16(m, 7 + m, 1.0 / np.sqrt(m))
     B = torch.full((m, m), float("nan"), dtype=torch.bfloat16, device=DEV)
-    b, c = -4.7750, 2.0315
-    mu.muon_test_poly_bf16(h, A, B, m, m, b, c)
+    a, b, c = 3.4445, -4.7750, 2.0315
+    mu.muon_test_poly_bf16(h, A, B, m, m, a, b, c)
     torch.cuda.synchronize()
     A64 = f64(A)
-    want = b * A64 + c * (A64 @ A64)
+    # the quintic's identity term sits on the diagonal: B X = a X + b A X + c A A X
+    want = a * np.eye(m) + b * A64 + c * (A64 @ A64)
     got = f64(B)
     assert np.isfinite(got).all()
     assert relF(got, want) < 4e-3
+    assert relF(np.diag(got), np.diag(want)) < 4e-3
+    off = ~np.eye(m, dtype=bool)
+    assert relF(got[off], want[off]) < 4e-3
     assert np.array_equal(got, got.T)
 
 
@@ -74,11 +78,10 @@ def test_update_phase(m, n, ldx, s):
     X = Xfull[:, :n]
     B = _sym_bf16(m, 5 + n, 1.0 / np.sqrt(m))
     Xo = torch.full((m, ldx), float("nan"), dtype=torch.bfloat16, device=DEV)
-    a = 3.4445
-    mu.muon_test_update_bf16(h, Xfull, B, Xo, m, n, ldx, m, a, s)
+    mu.muon_test_update_bf16(h, Xfull, B, Xo, m, n, ldx, m, s)
     torch.cuda.synchronize()
     X64, B64 = f64(X), f64(B)
-    want = s * (a * X64 + B64 @ X64)
+    want = s * (B64 @ X64)
     got = f64(Xo[:, :n])
     assert np.isfinite(got).all()
     assert relF(got, want) < 4e-3
