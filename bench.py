@@ -189,12 +189,13 @@ def main():
                     "frac": round(tf / peak_mm, 4)}
     dom = max(("gram", "poly", "update"), key=lambda p: phases[p][0])
     # memory-bound kernels.  Algorithmic bytes per element: momentum reads G
-    # and M, writes M and the bf16 Newton-Schulz input (G 4|2 + 4 + 4 + 2);
-    # apply reads W and O and writes W (4 + 2 + 4).  The momentum kernel also
-    # writes the transposed copy of the input (+2 B), counted in "actual".
+    # and M, writes M and the Newton-Schulz input (G 4|2 + 4 + 4 + 2|4);
+    # apply reads W and O and writes W (4 + 2|4 + 4).  The fp32 iteration
+    # also keeps the transposed copy of the input (+4 B), counted in "actual".
     g_bytes = 2 if wl.tensors[wl.muon[0].tensor].grad_dtype == torch.bfloat16 else 4
     ns_b = 4 if hpd["ns_dtype"] == "fp32" else 2
-    ew_bytes = {"momentum": ((g_bytes + 4 + 4 + ns_b) * el, (g_bytes + 4 + 4 + 2 * ns_b) * el),
+    ns_copies = 2 if hpd["ns_dtype"] == "fp32" else 1
+    ew_bytes = {"momentum": ((g_bytes + 4 + 4 + ns_b) * el, (g_bytes + 4 + 4 + ns_copies * ns_b) * el),
                 "apply": ((4 + ns_b + 4) * el, (4 + ns_b + 4) * el)}
     hbm = {}
     for ph, (b, b_act) in ew_bytes.items():
@@ -215,7 +216,7 @@ def main():
 
     dom_avg_ms = gemm[dom]["avg_ms"]
     traffic = _traffic_record("update_bf16_headline") if (dom == "update" and args.workload == "headline") else None
-    roofline = {"bound": "mfma", "kernel": "ns_update (X <- aX + BX)" if dom == "update" else dom,
+    roofline = {"bound": "mfma", "kernel": "ns_update (X <- B X, B = aI + bA + cAA)" if dom == "update" else dom,
                 "achieved": gemm[dom]["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
                 "frac": gemm[dom]["frac"], "traffic": traffic,
                 "per_launch_flops": per_launch_flops[dom], "avg_launch_ms": dom_avg_ms}
