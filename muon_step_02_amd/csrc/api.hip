@@ -42,6 +42,7 @@ struct TimedLaunch {
 
 struct muon_context {
     int device = 0;
+    int cus_per_xcd = 32;  // compute units per XCD (tile rounds)
     Slot slots[kSlots];
     int next = 0;
     bool profiling = false;
@@ -167,7 +168,7 @@ struct Plan {
 };
 
 muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
-                      uintptr_t ws, Plan& P) {
+                      uintptr_t ws, int cus, Plan& P) {
     if (!mats || n < 1) return MUON_ERR_INVALID_ARG;
     muon_status st = check_hparams(hp);
     if (st != MUON_OK) return st;
@@ -270,9 +271,11 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
             wn[k] = P.d[C.first + k].np;
             wm[k] = P.d[C.first + k].mp;
         }
-        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count);
-        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count);
-        C.xs_upd = xcd_split(tu.data(), wm.data(), C.count);
+        // quarter tiles for the short last round: large bf16 class only
+        const int quarters = (!P.ns_f32 && c == 0) ? 1 : 0;
+        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count, cus, quarters);
+        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count, cus, quarters);
+        C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters);
     }
 
     size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
@@ -370,6 +373,7 @@ muon_status muon_init(int device, muon_handle* out) {
     muon_context* h = new (std::nothrow) muon_context();
     if (!h) return MUON_ERR_HIP;
     h->device = device;
+    h->cus_per_xcd = prop.multiProcessorCount >= 8 ? prop.multiProcessorCount / 8 : 1;
     for (Slot& s : h->slots) {
         if (hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
             muon_destroy(h);
@@ -402,7 +406,7 @@ muon_status muon_workspace_size(muon_handle h, const muon_matrix* mats, int n,
                                 const muon_hparams* hp, size_t* bytes) {
     if (!h || !bytes) return MUON_ERR_INVALID_ARG;
     Plan P;
-    muon_status st = make_plan(mats, n, hp, false, 0, P);
+    muon_status st = make_plan(mats, n, hp, false, 0, h->cus_per_xcd, P);
     if (st != MUON_OK) return st;
     *bytes = P.total;
     return MUON_OK;
@@ -415,7 +419,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
     if (!workspace || ws % 256) return MUON_ERR_WORKSPACE;
     Plan P;
-    muon_status st = make_plan(mats, n, hp, true, ws, P);
+    muon_status st = make_plan(mats, n, hp, true, ws, h->cus_per_xcd, P);
     if (st != MUON_OK) return st;
     if (workspace_bytes < P.total) return MUON_ERR_WORKSPACE;
 
@@ -690,7 +694,7 @@ muon_status muon_test_gram_bf16(muon_handle h, const void* X, void* A, int64_t m
     if (st != MUON_OK) return st;
     if (!X || !A || ldx < n || lda < m || ldx % 8 || lda % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    return hip_status(launch_gram_bf16_single(X, A, (int)m, (int)n, ldx, lda, s2,
+    return hip_status(launch_gram_bf16_single(X, A, (int)m, (int)n, ldx, lda, s2, h->cus_per_xcd,
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -700,7 +704,7 @@ muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m
     if (st != MUON_OK) return st;
     if (!A || !B || lda < m || lda % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    return hip_status(launch_poly_bf16_single(A, B, (int)m, lda, a, b, c,
+    return hip_status(launch_poly_bf16_single(A, B, (int)m, lda, a, b, c, h->cus_per_xcd,
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -712,6 +716,7 @@ muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B, v
     if (!X || !B || !Xo || ldx < n || ldb < m || ldx % 8 || ldb % 8) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
     return hip_status(launch_update_bf16_single(X, B, Xo, (int)m, (int)n, ldx, ldb, s,
+                                                h->cus_per_xcd,
                                                 reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -460,13 +460,30 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
     }
 }
 
-// Tile of this workgroup under an XcdSplit (-1: none, exit).
-__device__ __forceinline__ int xcd_tile(const XcdSplit& xs) {
+// Task of this workgroup under an XcdSplit: a whole tile (quarter = -1) or
+// quarter q of a tile (rows (q >> 1), columns (q & 1) of its 2 x 2 split).
+// False: no task, exit.
+__device__ __forceinline__ bool xcd_task(const XcdSplit& xs, int& tile, int& quarter) {
     const int b = (int)blockIdx.x;
     const int x = b & 7;
-    const int t = xs.b[x] + (b >> 3);
-    return t < xs.b[x + 1] ? t : -1;
+    const int t = b >> 3;
+    const int whole = xs.b[x + 1] - xs.b[x] - xs.sub[x];
+    if (t < whole) {
+        tile = xs.b[x] + t;
+        quarter = -1;
+        return true;
+    }
+    const int u = t - whole;
+    if (u >= 4 * xs.sub[x]) return false;
+    tile = xs.b[x] + whole + (u >> 2);
+    quarter = u & 3;
+    return true;
 }
+
+// The configuration that computes a quarter of a C tile (same waves, same
+// threads, half the rows and columns).
+template <class C>
+using QuarterCfg = Cfg<C::BM / 2, C::BN / 2, C::WM, C::WN, C::BK, C::NS>;
 
 __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
     int t = (int)((sqrtf(8.f * (float)lt + 1.f) - 1.f) * 0.5f);
@@ -499,17 +516,22 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(xs);
-    if (tile < 0) return;
+    int tile, q;
+    if (!xcd_task(xs, tile, q)) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     int ti, tj;
     tri_index(tile - prefix[mi], ti, tj);
+    // a quarter above the diagonal of a diagonal tile is the mirror of the
+    // quarter below it
+    if (q >= 0 && ti == tj && (q >> 1) < (q & 1)) return;
+    // the tile (or quarter) holds part of the diagonal: stored once, no mirror
+    const bool on_diag = ti == tj && (q < 0 || (q >> 1) == (q & 1));
     const int64_t mp = d.mp, np = d.np;
     Epi ep;
     ep.out = reinterpret_cast<uint16_t*>(PHASE == GRAM ? d.a : d.b);
     ep.ld_out = mp;
-    ep.outT = (ti != tj) ? ep.out : nullptr;
+    ep.outT = on_diag ? nullptr : ep.out;
     ep.ld_outT = mp;
     const uint16_t* src;
     int64_t ld;
@@ -531,10 +553,17 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.coef_e = cb;
         ep.coef_acc = cc;
         ep.post = 1.f;
-        ep.diag = (ti == tj) ? ca : 0.f;
+        ep.diag = on_diag ? ca : 0.f;
     }
-    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+    if (q < 0) {
+        const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+        gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+    } else if constexpr (C::BM == 256) {
+        using Q = QuarterCfg<C>;
+        const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
+        const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
+        gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+    }
 }
 
 template <class C>
@@ -546,8 +575,8 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(xs);
-    if (tile < 0) return;
+    int tile, q;
+    if (!xcd_task(xs, tile, q)) return;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
@@ -567,8 +596,15 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     ep.coef_acc = 1.f;
     ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
     ep.diag = 0.f;
-    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, false, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
+    if (q < 0) {
+        const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+        gemm_tile<C, false, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
+    } else if constexpr (C::BM == 256) {
+        using Q = QuarterCfg<C>;
+        const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
+        const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
+        gemm_tile<Q, false, true>(B + r0 * mp, mp, X + c0, np, (int)mp, r0, c0, ep, st);
+    }
 }
 
 // single-matrix variants for the test hooks
@@ -582,24 +618,33 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(xs);
-    if (tile < 0) return;
+    int tile, q;
+    if (!xcd_task(xs, tile, q)) return;
     int ti, tj;
     tri_index(tile, ti, tj);
+    if (q >= 0 && ti == tj && (q >> 1) < (q & 1)) return;
+    const bool on_diag = ti == tj && (q < 0 || (q >> 1) == (q & 1));
     Epi ep;
     ep.out = out;
     ep.ld_out = ld_out;
-    ep.outT = (ti != tj) ? out : nullptr;
+    ep.outT = on_diag ? nullptr : out;
     ep.ld_outT = ld_out;
     if (PHASE == GRAM) {
         ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = sq; ep.post = 1.f;
         ep.diag = 0.f;
     } else {
         ep.E = src; ep.ld_e = ld; ep.coef_e = cb; ep.coef_acc = cc; ep.post = 1.f;
-        ep.diag = (ti == tj) ? ca : 0.f;
+        ep.diag = on_diag ? ca : 0.f;
     }
-    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+    if (q < 0) {
+        const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+        gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+    } else {
+        using Q = QuarterCfg<C>;
+        const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
+        const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
+        gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+    }
 }
 
 template <class C>
@@ -612,15 +657,22 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
     __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
-    const int tile = xcd_tile(xs);
-    if (tile < 0) return;
+    int tile, q;
+    if (!xcd_task(xs, tile, q)) return;
     int ti, tj;
     grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
     Epi ep;
     ep.out = Xo; ep.ld_out = ldx; ep.outT = nullptr; ep.ld_outT = 0;
     ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = 1.f; ep.post = s; ep.diag = 0.f;
-    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-    gemm_tile<C, false, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
+    if (q < 0) {
+        const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+        gemm_tile<C, false, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
+    } else {
+        using Q = QuarterCfg<C>;
+        const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
+        const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
+        gemm_tile<Q, false, true>(B + r0 * ldb, ldb, X + c0, ldx, m, r0, c0, ep, st);
+    }
 }
 
 inline int xcd_grid(const XcdSplit& xs) { return 8 * (xs.per > 0 ? xs.per : 1); }
@@ -636,7 +688,7 @@ int gemm_tile_bf16(int small) { return small ? SmallCfg::BM : SymCfg::BM; }
 int upd_tile_m_bf16(int small) { return small ? SmallCfg::BM : UpdCfg::BM; }
 int upd_tile_n_bf16(int small) { return small ? SmallCfg::BN : UpdCfg::BN; }
 
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n) {
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters) {
     XcdSplit xs;
     int64_t total_w = 0, total_t = 0;
     for (int k = 0; k < n; ++k) {
@@ -665,7 +717,12 @@ XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n) {
     xs.per = 0;
     for (int i = 0; i < 8; ++i) {
         if (xs.b[i + 1] < xs.b[i]) xs.b[i + 1] = xs.b[i];
-        if (xs.b[i + 1] - xs.b[i] > xs.per) xs.per = xs.b[i + 1] - xs.b[i];
+        const int T = xs.b[i + 1] - xs.b[i];
+        // last round of R tiles on `cus` CUs: as 4R quarter tiles when R <= cus/2
+        const int R = cus > 0 ? T % cus : 0;
+        xs.sub[i] = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
+        const int tasks = T + 3 * xs.sub[i];
+        if (tasks > xs.per) xs.per = tasks;
     }
     return xs;
 }
@@ -698,11 +755,11 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 }
 
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
-                                   float s2, hipStream_t st) {
+                                   float s2, int cus, hipStream_t st) {
     const int T = m / SymCfg::BM;
     const int32_t total = T * (T + 1) / 2;
     const int64_t w = 1;
-    const XcdSplit xs = xcd_split(&total, &w, 1);
+    const XcdSplit xs = xcd_split(&total, &w, 1, cus, 1);
     ns_sym_single<SymCfg, GRAM><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), ldx, n, reinterpret_cast<uint16_t*>(A), lda, s2, 0.f,
         0.f, 0.f, xs);
@@ -710,11 +767,11 @@ hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t
 }
 
 hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float a, float b,
-                                   float c, hipStream_t st) {
+                                   float c, int cus, hipStream_t st) {
     const int T = m / SymCfg::BM;
     const int32_t total = T * (T + 1) / 2;
     const int64_t w = 1;
-    const XcdSplit xs = xcd_split(&total, &w, 1);
+    const XcdSplit xs = xcd_split(&total, &w, 1, cus, 1);
     ns_sym_single<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(A), lda, m, reinterpret_cast<uint16_t*>(B), lda, 1.f, a,
         b, c, xs);
@@ -722,11 +779,11 @@ hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, f
 }
 
 hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
-                                     int64_t ldx, int64_t ldb, float s, hipStream_t st) {
+                                     int64_t ldx, int64_t ldb, float s, int cus, hipStream_t st) {
     const int tiles = (m / UpdCfg::BM) * (n / UpdCfg::BN);
     const int32_t total = tiles;
     const int64_t w = 1;
-    const XcdSplit xs = xcd_split(&total, &w, 1);
+    const XcdSplit xs = xcd_split(&total, &w, 1, cus, 1);
     ns_update_single<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
         reinterpret_cast<uint16_t*>(Xo), m, n, ldx, ldb, s, xs);

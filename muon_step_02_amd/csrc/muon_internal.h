@@ -125,14 +125,22 @@ hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int 
 // Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
 // b % 8).  XcdSplit gives XCD x the contiguous tile range [b[x], b[x+1]):
 // tiles that share operand slabs then share one L2, and the ranges are cut
-// at equal work (tiles weighted by their K), not equal tile counts.  The
-// grid is 8 * per workgroups, per = the largest range.
+// at equal work (tiles weighted by their K), not equal tile counts.
+//
+// An XCD runs its tiles in rounds of one tile per CU.  When the last round
+// would leave at least half of the CUs idle, its sub[x] tiles are run as
+// four quarter tiles each instead (task order: whole tiles, then the quarters
+// of the remaining tiles, four consecutive tasks per tile).  The grid is
+// 8 * per workgroups, per = the largest task count of an XCD.
 struct XcdSplit {
     int32_t b[9];
     int32_t per;
+    int32_t sub[8];
 };
-// Split `ntiles[k]` tiles of weight `weight[k]` (matrix order) into 8 ranges.
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n);
+// Split `ntiles[k]` tiles of weight `weight[k]` (matrix order) into 8 ranges;
+// with `quarters`, the short last round of each range is split as above
+// (cus = compute units per XCD).
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters);
 
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st);
@@ -154,11 +162,11 @@ constexpr int kTileF32 = 64;
 
 // single-phase test hooks (one matrix, caller buffers)
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
-                                   float s2, hipStream_t st);
+                                   float s2, int cus, hipStream_t st);
 hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, float a, float b,
-                                   float c, hipStream_t st);
+                                   float c, int cus, hipStream_t st);
 hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
-                                     int64_t ldx, int64_t ldb, float s, hipStream_t st);
+                                     int64_t ldx, int64_t ldb, float s, int cus, hipStream_t st);
 
 // AdamW: tensors travel in kernel arguments, kAdamwGroup per launch.
 constexpr int kAdamwGroup = 32;

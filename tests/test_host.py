@@ -181,13 +181,15 @@ XCD_SPLIT_TEST = r"""
 #include <vector>
 #include <algorithm>
 namespace muon {
-struct XcdSplit { int32_t b[9]; int32_t per; };
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n);
+struct XcdSplit { int32_t b[9]; int32_t per; int32_t sub[8]; };
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters);
 }
 int main() {
     srand(7);
     for (int trial = 0; trial < 20000; ++trial) {
         int n = 1 + rand() % 12;
+        const int cus = (trial & 1) ? 32 : 1 + rand() % 40;
+        const int quarters = (trial >> 1) & 1;
         std::vector<int32_t> t(n);
         std::vector<int64_t> w(n);
         int64_t total_t = 0, total_w = 0, wmax = 0;
@@ -196,12 +198,17 @@ int main() {
             w[k] = 1 + rand() % 256;
             total_t += t[k]; total_w += t[k] * w[k]; wmax = std::max(wmax, w[k]);
         }
-        muon::XcdSplit xs = muon::xcd_split(t.data(), w.data(), n);
+        muon::XcdSplit xs = muon::xcd_split(t.data(), w.data(), n, cus, quarters);
         if (xs.b[0] != 0 || xs.b[8] != total_t) { printf("bad ends %d\n", trial); return 1; }
         int per = 0;
         for (int x = 0; x < 8; ++x) {
-            if (xs.b[x + 1] < xs.b[x]) { printf("not monotone %d\n", trial); return 1; }
-            per = std::max(per, xs.b[x + 1] - xs.b[x]);
+            const int T = xs.b[x + 1] - xs.b[x];
+            if (T < 0) { printf("not monotone %d\n", trial); return 1; }
+            const int R = T % cus;
+            // quarters only on the short last round, and only when asked for
+            const int want = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
+            if (xs.sub[x] != want) { printf("sub %d x=%d %d/%d\n", trial, x, xs.sub[x], want); return 1; }
+            per = std::max(per, T - xs.sub[x] + 4 * xs.sub[x]);
         }
         if (per != xs.per) { printf("per %d\n", trial); return 1; }
         // work of each range within one tile of the ideal eighth
