@@ -28,10 +28,14 @@
 // (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation).  K advances in slabs of 64: operand slabs are copied
 // global->LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
-// staging) into two LDS stages, so the copy of slab k+1 overlaps the MFMAs
-// on slab k.  The epilogue goes through LDS so that every global access is a
-// coalesced 16-byte one.  LDS rows are XOR-swizzled (see swz) so fragment
-// reads are free of bank conflicts.
+// staging) into LDS stages (two for 256 x 256 tiles, four for 128 x 128), so
+// the copies of later slabs overlap the MFMAs on slab k.  The epilogue goes
+// through LDS so that every global access is a coalesced 16-byte one.  LDS
+// rows are XOR-swizzled (see swz, swzk) so fragment reads are free of bank
+// conflicts.
+//
+// Each XCD takes a contiguous range of tiles; a short last round is run as
+// quarter tiles (see XcdSplit).
 //
 // Grouped launch: one launch per phase covers every matrix; workgroup ->
 // (matrix, tile) through prefix sums of tiles per matrix.
@@ -48,11 +52,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 enum { GRAM = 0, POLY = 1, UPDATE = 2 };
 
+// LDS is four 32 KB arrays (see Stages).
+constexpr int kLdsArr = 16384;  // bf16 elements per array
+
 template <int BM_, int BN_, int WM_, int WN_, int BK_ = 64, int NS_ = 2>
 struct Cfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
     static constexpr int BK = BK_;   // k per LDS stage (32 or 64)
-    static constexpr int NS = NS_;   // LDS stages (2..4)
+    static constexpr int NS = NS_;   // LDS stages
     static constexpr int NW = WM * WN;
     static constexpr int NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -61,18 +68,53 @@ struct Cfg {
     static constexpr int RPI = 64 / CH;        // rows per global_load_lds (1 KB)
     static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
     static constexpr int LPS = ((BM + BN) / RPI) / NW;  // slab copies per stage per wave
-    // epilogue: bands of RB rows staged as fp32 in one stage buffer; the row
-    // stride puts rows r and r + 4 (the two half-waves of an accumulator
-    // store) 32 banks apart
-    static constexpr int LDW = BN + 8;
-    static constexpr int RB = (32 * LDW * 4 <= STAGE * 2) ? 32 : 16;
-    static_assert(RB * LDW * 4 <= STAGE * 2, "epilogue band must fit one stage");
+    // a stage is one LDS array (P slab, then Q slab) or, when each slab fills
+    // an array by itself, two (P, Q)
+    static constexpr int SPLIT = STAGE > kLdsArr ? 1 : 0;
+    static constexpr int NARR = SPLIT ? 2 * NS : NS;  // LDS arrays used
+    // epilogue: bands of RB rows staged as fp32 in array 0
+    static constexpr int RB = 32;  // = the MFMA tile height: a band is one row block
+    static_assert(SPLIT ? (BM * BK == kLdsArr && BN * BK == kLdsArr) : STAGE <= kLdsArr,
+                  "a stage is one array, or one array per operand");
+    static_assert(NARR <= 4, "four LDS arrays");
+    static_assert(RB * BN * 4 <= kLdsArr * 2, "epilogue band must fit one array");
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 MFMA tile");
     static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "slab rows must split over waves");
     static_assert((RB * BN / 8) % NT == 0 && (BN * RB / 8) % NT == 0, "epilogue chunks must split");
 };
+
+// LDS: four 32 KB arrays, each its own __shared__ variable (declared in the
+// kernel) so the compiler can tell that a copy into one array does not alias
+// the fragment reads from another; otherwise it waits for every outstanding
+// copy before each read and the prefetch is lost.  A 256 x 256 tile keeps two
+// stages of two arrays (P slab, Q slab); a 128 x 128 tile keeps up to four
+// stages of one array each.
+struct Stages {
+    uint16_t* s[4];
+};
+
+__device__ __forceinline__ uint16_t* lds_arr(const Stages& st, int i) {
+    return i == 0 ? st.s[0] : i == 1 ? st.s[1] : i == 2 ? st.s[2] : st.s[3];
+}
+template <class C>
+__device__ __forceinline__ uint16_t* stage_p(const Stages& st, int i) {
+    return C::SPLIT ? lds_arr(st, 2 * i) : lds_arr(st, i);
+}
+template <class C>
+__device__ __forceinline__ uint16_t* stage_q(const Stages& st, int i) {
+    return C::SPLIT ? lds_arr(st, 2 * i + 1) : lds_arr(st, i) + C::BM * C::BK;
+}
+
+// Epilogue band buffer (fp32, RB x BN, in array 0), unpadded: column c of row
+// r sits at c ^ ((r & 4) << 3), so the two half-waves of an accumulator store
+// (rows r and r + 4) land 32 banks apart, and runs of 8 columns stay
+// contiguous.
+template <class C>
+__device__ __forceinline__ int sbi(int r, int c) {
+    return r * C::BN + (c ^ ((r & 4) << 3));
+}
 
 // LDS slab layout: row r holds BK bf16 = CH chunks of 16 bytes; logical chunk
 // c of row r sits at chunk position c ^ swz(r).  A fragment read has 16
@@ -186,12 +228,12 @@ struct Epi {
 template <class C, bool QKN>
 __device__ __forceinline__ void load_stage(const uint16_t* __restrict__ P0, int64_t ldp,
                                            const uint16_t* __restrict__ Q0, int64_t ldq,
-                                           int64_t k0, uint16_t* dst, int wave, int lane) {
-    load_slab<C, C::BM>(P0 + k0, ldp, dst, wave, lane);
+                                           int64_t k0, const Stages& st, int i, int wave, int lane) {
+    load_slab<C, C::BM>(P0 + k0, ldp, stage_p<C>(st, i), wave, lane);
     if (QKN)
-        load_slab_kn<C>(Q0 + k0 * ldq, ldq, dst + C::BM * C::BK, wave, lane);
+        load_slab_kn<C>(Q0 + k0 * ldq, ldq, stage_q<C>(st, i), wave, lane);
     else
-        load_slab<C, C::BN>(Q0 + k0, ldq, dst + C::BM * C::BK, wave, lane);
+        load_slab<C, C::BN>(Q0 + k0, ldq, stage_q<C>(st, i), wave, lane);
 }
 
 // Fragments of MFMA k-step kk (16 deep) of one LDS slab: FM row blocks of
@@ -202,9 +244,10 @@ struct Frags {
 };
 
 template <class C, bool QKN>
-__device__ __forceinline__ void read_frags(const uint16_t* sp, int kk, int wm, int wn, int frow,
-                                           int khalf, int lane, Frags<C>& f) {
-    const uint16_t* sq = sp + C::BM * C::BK;
+__device__ __forceinline__ void read_frags(const Stages& st, int i, int kk, int wm, int wn,
+                                           int frow, int khalf, int lane, Frags<C>& f) {
+    const uint16_t* sp = stage_p<C>(st, i);
+    const uint16_t* sq = stage_q<C>(st, i);
     const int lch = 2 * kk + khalf;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
@@ -245,18 +288,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// The LDS stages.  Each is its own __shared__ variable (declared in the
-// kernel) so the compiler can tell that the copy into one stage does not
-// alias the fragment reads from another; otherwise it waits for every
-// outstanding copy before each read and the prefetch is lost.
-struct Stages {
-    uint16_t* s[4];
-};
-
-template <class C>
-__device__ __forceinline__ uint16_t* stage(const Stages& st, int i) {
-    return i == 0 ? st.s[0] : i == 1 ? st.s[1] : i == 2 ? st.s[2] : st.s[3];
-}
 
 // E chunks of one epilogue band, in the order the combine pass reads them.
 template <class C, int QN>
@@ -306,13 +337,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
     for (int u = 0; u < C::NS; ++u) {
         if (u < KT) {
-            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, stage<C>(st, u), wave, lane);
+            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, st, u, wave, lane);
         }
     }
     if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * C::LPS>(); else wait_vmcnt<0>();
     __syncthreads();
     Frags<C> f[2];
-    read_frags<C, QKN>(stage<C>(st, 0), 0, wm, wn, frow, khalf, lane, f[0]);
+    read_frags<C, QKN>(st, 0, 0, wm, wn, frow, khalf, lane, f[0]);
 
     for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
 #pragma unroll
@@ -322,7 +353,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     if (kk + 1 < KS) {
-                        read_frags<C, QKN>(stage<C>(st, u), kk + 1, wm, wn, frow, khalf, lane,
+                        read_frags<C, QKN>(st, u, kk + 1, wm, wn, frow, khalf, lane,
                                            f[(kk + 1) & 1]);
                     } else {
                         // slab kt + 1 has landed once only the copies of the
@@ -334,10 +365,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                         __syncthreads();
                         if (kt + C::NS < KT) {
                             load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)(kt + C::NS) * C::BK,
-                                               stage<C>(st, u), wave, lane);
+                                               st, u, wave, lane);
                         }
-                        read_frags<C, QKN>(stage<C>(st, (u + 1) % C::NS), 0, wm, wn, frow, khalf,
-                                           lane, f[0]);
+                        read_frags<C, QKN>(st, (u + 1) % C::NS, 0, wm, wn, frow, khalf, lane, f[0]);
                     }
                     mfma_frags<C>(acc, f[kk & 1]);
                     // the k-major reads are twice as many: front-load them
@@ -356,7 +386,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
     // The band loop is unrolled so the compiler can count outstanding memory
     // operations exactly: no wait ever covers the stores of earlier bands, and
     // E is loaded one band ahead so its latency hides behind the LDS work.
-    float* sb = reinterpret_cast<float*>(st.s[0]);
+    float* sb = reinterpret_cast<float*>(lds_arr(st, 0));
     constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
     uint4 ecur[QN], enxt[QN];
     wait_vmcnt<0>();  // every slab copy has landed: the band buffer is free
@@ -365,36 +395,17 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
     for (int band = 0; band < C::BM / C::RB; ++band) {
         if (HAS_E && band + 1 < C::BM / C::RB) load_e_band<C, QN>(ep, row0, col0, band + 1, enxt);
         __syncthreads();
+        // the band is MFMA row block i of the waves with wm * TM + 32 i == 32 band
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
+            if (wm * C::TM + i * 32 == band * C::RB) {
 #pragma unroll
-            for (int h = 0; h < 32 / C::RB + (C::RB > 32 ? 1 : 0); ++h) {
-                // fragment i covers tile rows [fr0, fr0 + 32); with RB = 16
-                // it spans two bands (register groups r >> 2 in {0,1} / {2,3})
-                const int fr0 = wm * C::TM + i * 32;
-                if (C::RB == 32) {
-                    if (fr0 == band * C::RB) {
+                for (int j = 0; j < C::FN; ++j) {
+                    const int c = wn * C::TN + j * 32 + frow;
 #pragma unroll
-                        for (int j = 0; j < C::FN; ++j) {
-                            const int c = wn * C::TN + j * 32 + frow;
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3);
-                                sb[rr * C::LDW + c] = acc[i][j][r];
-                            }
-                        }
-                    }
-                } else {
-                    if (fr0 + 16 * h == band * C::RB) {
-#pragma unroll
-                        for (int j = 0; j < C::FN; ++j) {
-                            const int c = wn * C::TN + j * 32 + frow;
-#pragma unroll
-                            for (int r = 8 * h; r < 8 * h + 8; ++r) {
-                                const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3) - 16 * h;
-                                sb[rr * C::LDW + c] = acc[i][j][r];
-                            }
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3);
+                        sb[sbi<C>(rr, c)] = acc[i][j][r];
                     }
                 }
             }
@@ -405,8 +416,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
         for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
             const int ch = q * C::NT + threadIdx.x;
             const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
-            const float4 a0 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8);
-            const float4 a1 = *reinterpret_cast<const float4*>(sb + rr * C::LDW + c8 + 4);
+            const float4 a0 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8));
+            const float4 a1 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8) + 4);
             float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
             if (HAS_E) {
                 const uint32_t ew[4] = {ecur[q].x, ecur[q].y, ecur[q].z, ecur[q].w};
@@ -432,8 +443,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
             o.w = pack2(v[6], v[7]);
             gst(reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8), o);
             if (ep.outT) {
-                *reinterpret_cast<float4*>(sb + rr * C::LDW + c8) = make_float4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<float4*>(sb + rr * C::LDW + c8 + 4) = make_float4(v[4], v[5], v[6], v[7]);
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
             }
         }
         if (ep.outT) {
@@ -444,7 +455,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                 const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = sb[(i8 + e) * C::LDW + c];
+                for (int e = 0; e < 8; ++e) v[e] = sb[sbi<C>(i8 + e, c)];
                 uint4 o;
                 o.x = pack2(v[0], v[1]);
                 o.y = pack2(v[2], v[3]);
@@ -483,7 +494,13 @@ __device__ __forceinline__ bool xcd_task(const XcdSplit& xs, int& tile, int& qua
 // The configuration that computes a quarter of a C tile (same waves, same
 // threads, half the rows and columns).
 template <class C>
-using QuarterCfg = Cfg<C::BM / 2, C::BN / 2, C::WM, C::WN, C::BK, C::NS>;
+using QuarterCfg = Cfg<C::BM / 2, C::BN / 2, C::WM, C::WN, C::BK, 4>;
+
+// LDS arrays a kernel on tiles of C needs (with quarter tiles for 256 x 256).
+template <class C>
+constexpr int lds_arrays() {
+    return C::BM == 256 ? (C::NARR > QuarterCfg<C>::NARR ? C::NARR : QuarterCfg<C>::NARR) : C::NARR;
+}
 
 __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
     int t = (int)((sqrtf(8.f * (float)lt + 1.f) - 1.f) * 0.5f);
@@ -511,10 +528,11 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
                                                        const int32_t* __restrict__ prefix,
                                                        XcdSplit xs, int it, float ca, float cb,
                                                        float cc) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    constexpr int NA = lds_arrays<C>();
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[NA > 1 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[NA > 2 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[NA > 3 ? kLdsArr : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
     int tile, q;
     if (!xcd_task(xs, tile, q)) return;
@@ -570,10 +588,11 @@ template <class C>
 __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restrict__ descs, int n,
                                                           const int32_t* __restrict__ prefix,
                                                           XcdSplit xs, int it) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    constexpr int NA = lds_arrays<C>();
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[NA > 1 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[NA > 2 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[NA > 3 ? kLdsArr : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
     int tile, q;
     if (!xcd_task(xs, tile, q)) return;
@@ -613,10 +632,11 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
                                                        int K, uint16_t* out, int64_t ld_out,
                                                        float sq, float ca, float cb, float cc,
                                                        XcdSplit xs) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    constexpr int NA = lds_arrays<C>();
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[NA > 1 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[NA > 2 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[NA > 3 ? kLdsArr : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
     int tile, q;
     if (!xcd_task(xs, tile, q)) return;
@@ -652,10 +672,11 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
                                                           const uint16_t* __restrict__ B,
                                                           uint16_t* Xo, int m, int n, int64_t ldx,
                                                           int64_t ldb, float s, XcdSplit xs) {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NS > 2 ? C::STAGE : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NS > 3 ? C::STAGE : 8];
+    constexpr int NA = lds_arrays<C>();
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[NA > 1 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[NA > 2 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[NA > 3 ? kLdsArr : 8];
     const Stages st{{lds0, lds1, lds2, lds3}};
     int tile, q;
     if (!xcd_task(xs, tile, q)) return;
