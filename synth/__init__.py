@@ -281,4 +281,7 @@ def headline(n=8, dim=4096):
 
 
 WORKLOADS = {"c0": config0, "c1": config1, "c2": config2, "c3": config3, "c4": config4,
-             "headline": headline}
+             "headline": headline,
+             # the same matrices, fewer of them: one 4096^2 matrix leaves most
+             # of the chip idle (136 Gram tiles against 256 CUs)
+             "headline-1": lambda: headline(n=1), "headline-2": lambda: headline(n=2)}

@@ -66,6 +66,33 @@ def hp_from(muon_hp, **over):
                            scale_mode=d["scale_mode"], coeffs=d.get("coeffs"))
 
 
+def recipe_floor_output(Y, steps=5, eps=1e-7, coeffs=None):
+    """The Newton-Schulz recipe run the way a plain bf16 implementation runs
+    it: every tensor held in bf16, products accumulated in fp32 and rounded,
+    every elementwise result rounded ("About Muon: Why Not Adam", section
+    "Making It Actually Run", iterated in bf16 as "The Optimizer Wars ...",
+    section "What is Muon?" describes).  On the CPU, on the NS input Y.  Its
+    distance to the oracle is the error floor such an implementation has on
+    this input; reported beside the kernels' error, never used as a
+    reference."""
+    def r(t):
+        return t.to(torch.bfloat16).to(torch.float32)
+    X = r(torch.from_numpy(np.ascontiguousarray(Y, dtype=np.float32)))
+    tr = X.shape[0] > X.shape[1]
+    if tr:
+        X = X.T.contiguous()
+    X = r(X / (r(torch.linalg.norm(X)) + eps))
+    sched = ([tuple(c) for c in np.asarray(coeffs).reshape(-1, 3)] if coeffs is not None
+             else [oracle.MUON_COEFFS] * steps)
+    for a, b, c in sched:
+        A = r(X @ X.T)
+        B = r(r(b * A) + r(c * r(A @ A)))
+        X = r(r(a * X) + r(B @ X))
+    if tr:
+        X = X.T
+    return X.double().numpy()
+
+
 def oracle_kwargs(muon_hp, **over):
     d = dict(muon_hp)
     d.update(over)
