@@ -160,11 +160,11 @@ typedef struct {
 } adamw_hparams;
 
 /* Bind a handle to HIP device `device`.  Fails with
- * MUON_ERR_UNSUPPORTED_DEVICE unless the device is gfx950.  Allocates the
- * handle's pinned host descriptor slots.  Release with muon_destroy. */
+ * MUON_ERR_UNSUPPORTED_DEVICE unless the device is gfx950.  Release with
+ * muon_destroy. */
 muon_status muon_init(int device, muon_handle* out);
 
-/* Free the handle (waits for the handle's pending descriptor copies). */
+/* Free the handle (waits for the events of an unfinished profile). */
 muon_status muon_destroy(muon_handle h);
 
 /* Bytes of device workspace muon_step_batched needs for exactly these
@@ -177,7 +177,12 @@ muon_status muon_workspace_size(muon_handle h, const muon_matrix* mats, int n,
  * device's null stream).  `workspace` is caller-owned device memory of at
  * least muon_workspace_size bytes, 256-byte aligned, used only by this call's
  * kernels; it must not be shared by calls that may run concurrently.  The
- * descriptor array is host memory, read during the call only.  Rejects:
+ * descriptor array is host memory, read during the call only: the table the
+ * kernels read is carried into the workspace in kernel arguments.  The call
+ * enqueues work on `stream` and returns; it never waits on the host and keeps
+ * no reference to host memory, so it may be captured in a graph (a replay
+ * runs the captured shapes and pointers on the buffers' contents at replay
+ * time).  Rejects:
  * n < 1, rows or cols < 1, ld < cols, a null param/grad/momentum, an unknown
  * dtype or mode, ns_steps < 1, lr/momentum non-finite, overlapping
  * param/grad/momentum ranges within a matrix, a small or null workspace,

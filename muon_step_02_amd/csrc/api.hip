@@ -23,15 +23,7 @@ using namespace muon;
 
 namespace {
 
-constexpr int kSlots = 8;
 constexpr float kMuonA = 3.4445f, kMuonB = -4.7750f, kMuonC = 2.0315f;
-
-struct Slot {
-    void* host = nullptr;
-    size_t cap = 0;
-    hipEvent_t ev = nullptr;
-    bool pending = false;
-};
 
 }  // namespace
 
@@ -43,8 +35,7 @@ struct TimedLaunch {
 struct muon_context {
     int device = 0;
     int cus_per_xcd = 32;  // compute units per XCD (tile rounds)
-    Slot slots[kSlots];
-    int next = 0;
+    std::vector<char> table;  // host image of the descriptor table (reused)
     bool profiling = false;
     std::vector<TimedLaunch> timed;     // recorded since the last collect
     std::vector<hipEvent_t> event_pool;  // timing events ready for reuse
@@ -374,12 +365,6 @@ muon_status muon_init(int device, muon_handle* out) {
     if (!h) return MUON_ERR_HIP;
     h->device = device;
     h->cus_per_xcd = prop.multiProcessorCount >= 8 ? prop.multiProcessorCount / 8 : 1;
-    for (Slot& s : h->slots) {
-        if (hipEventCreateWithFlags(&s.ev, hipEventDisableTiming) != hipSuccess) {
-            muon_destroy(h);
-            return MUON_ERR_HIP;
-        }
-    }
     *out = h;
     return MUON_OK;
 }
@@ -387,11 +372,6 @@ muon_status muon_init(int device, muon_handle* out) {
 muon_status muon_destroy(muon_handle h) {
     if (!h) return MUON_ERR_INVALID_ARG;
     DeviceGuard g(h->device);
-    for (Slot& s : h->slots) {
-        if (s.pending) (void)hipEventSynchronize(s.ev);
-        if (s.host) (void)hipHostFree(s.host);
-        if (s.ev) (void)hipEventDestroy(s.ev);
-    }
     for (TimedLaunch& t : h->timed) {
         (void)hipEventSynchronize(t.stop);
         h->event_pool.push_back(t.start);
@@ -426,33 +406,19 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     DeviceGuard g(h->device);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-    // descriptor table + prefixes -> pinned slot -> workspace
-    Slot& slot = h->slots[h->next];
-    h->next = (h->next + 1) % kSlots;
-    if (slot.pending) {
-        if (hipEventSynchronize(slot.ev) != hipSuccess) return MUON_ERR_HIP;
-        slot.pending = false;
-    }
-    if (slot.cap < P.table_bytes) {
-        if (slot.host) (void)hipHostFree(slot.host);
-        slot.host = nullptr;
-        slot.cap = 0;
-        const size_t cap = std::max<size_t>(P.table_bytes, 64 * 1024);
-        if (hipHostMalloc(&slot.host, cap, hipHostMallocDefault) != hipSuccess) return MUON_ERR_HIP;
-        slot.cap = cap;
-    }
-    char* hb = reinterpret_cast<char*>(slot.host);
-    memset(hb, 0, P.table_bytes);
+    // descriptor table + prefixes: built on the host, carried to the
+    // workspace in kernel arguments.  Nothing waits on the host and nothing
+    // refers to host memory after the call, so the step can be captured in a
+    // graph and replayed.
+    h->table.assign(P.table_bytes, 0);
+    char* hb = h->table.data();
     memcpy(hb, P.d.data(), (size_t)n * sizeof(MatDesc));
     memcpy(hb + P.off_pew, P.pew.data(), (size_t)(n + 1) * 4);
     for (const ClassPlan& c : P.cls) {
         memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
     }
-    if (hipMemcpyAsync(workspace, hb, P.table_bytes, hipMemcpyHostToDevice, s) != hipSuccess)
-        return MUON_ERR_HIP;
-    if (hipEventRecord(slot.ev, s) != hipSuccess) return MUON_ERR_HIP;
-    slot.pending = true;
+    if (launch_table_upload(hb, P.table_bytes, workspace, s) != hipSuccess) return MUON_ERR_HIP;
 
     const MatDesc* dd = reinterpret_cast<const MatDesc*>(workspace);
     Prefix pf;  // elementwise kernels: all matrices

@@ -23,6 +23,8 @@
 // Each workgroup of the Muon kernels owns one 64 x 64 tile of one weight;
 // 256 threads, each thread four rows of four consecutive columns, so a wave
 // reads four 256-byte row segments per instruction (fp32).
+#include <string.h>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -339,6 +341,16 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
         apply_tile<false, NS_F32>(d, lt, parity, decay, step, qk_tau, tileT);
 }
 
+// ------------------------------------------------------ table upload ----
+
+struct TableChunk {
+    uint32_t w[kTableChunkWords];
+};
+
+__global__ __launch_bounds__(256) void table_upload_kernel(TableChunk c, uint32_t* dst, int nwords) {
+    for (int i = threadIdx.x; i < nwords; i += 256) gst(dst + i, c.w[i]);
+}
+
 // ---------------------------------------------------------------- AdamW ----
 
 __device__ __forceinline__ void adamw_elem(float& th, float g, float& m, float& v, float lr,
@@ -490,6 +502,21 @@ hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int 
     else
         apply_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr, qk_tau);
     return hipGetLastError();
+}
+
+hipError_t launch_table_upload(const void* host, size_t bytes, void* dst, hipStream_t st) {
+    const uint32_t* src = static_cast<const uint32_t*>(host);
+    const size_t words = bytes / 4;
+    for (size_t w0 = 0; w0 < words; w0 += kTableChunkWords) {
+        const int nw = (int)(words - w0 < (size_t)kTableChunkWords ? words - w0 : kTableChunkWords);
+        TableChunk c;
+        memcpy(c.w, src + w0, (size_t)nw * 4);
+        if (nw < kTableChunkWords) memset(c.w + nw, 0, (size_t)(kTableChunkWords - nw) * 4);
+        table_upload_kernel<<<1, 256, 0, st>>>(c, static_cast<uint32_t*>(dst) + w0, nw);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,

@@ -111,6 +111,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---- launch wrappers ------------------------------------------------------
 // All return hipGetLastError() after the launch.
+
+// Copy `bytes` (a multiple of 4) of host data to device memory `dst` in
+// kernel arguments, kTableChunkWords words per launch.
+constexpr int kTableChunkWords = 512;
+hipError_t launch_table_upload(const void* host, size_t bytes, void* dst, hipStream_t st);
 hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
                            int nesterov, int ns_f32, hipStream_t st);
 hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t st);

@@ -1,0 +1,86 @@
+"""The Muon step and the clipped AdamW step captured in a HIP graph (through
+torch.cuda.graph) and replayed: each replay must equal, bit for bit, the same
+calls made eagerly on a copy of the state, with eager work between replays
+that changes the gradients the graph reads.  The library waits on nothing on
+the host and refers to no host memory after a call, so a captured step
+replays on whatever the buffers hold at replay time."""
+
+import pytest
+import torch
+
+import synth
+import muon_step_02_amd as mu
+from harness import Handle, hp_from
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# mixed shapes: square, wide, tall (transposed), and a small-class block
+SHAPES = [(512, 384), (256, 768), (1024, 640), (128, 512)]
+ADAMW_SHAPES = [(1000,), (64, 33)]
+
+
+def _state(seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    W = [torch.randn(s, generator=g, device=DEV) * 0.02 for s in SHAPES]
+    G = [torch.randn(s, generator=g, device=DEV) for s in SHAPES]
+    M = [torch.zeros(s, device=DEV) for s in SHAPES]
+    P = [torch.randn(s, generator=g, device=DEV) for s in ADAMW_SHAPES]
+    Q = [torch.randn(s, generator=g, device=DEV) * 3.0 for s in ADAMW_SHAPES]
+    m = [torch.zeros(s, device=DEV) for s in ADAMW_SHAPES]
+    v = [torch.zeros(s, device=DEV) for s in ADAMW_SHAPES]
+    return dict(W=W, G=G, M=M, P=P, Q=Q, m=m, v=v)
+
+
+class Step:
+    """One optimizer step over a state: Muon on the matrices, clipped AdamW
+    on the rest, all on the current stream."""
+
+    def __init__(self, h, st):
+        self.h = h
+        self.st = st
+        self.hp = hp_from(synth.MUON_DEFAULT)
+        self.mats = [mu.muon_matrix(W, G, M) for W, G, M in zip(st["W"], st["G"], st["M"])]
+        self.ws = torch.empty(mu.muon_workspace_size(h, self.mats, self.hp), dtype=torch.uint8,
+                              device=DEV)
+        self.ts = [mu.adamw_tensor(p, q, a, b) for p, q, a, b in zip(st["P"], st["Q"], st["m"], st["v"])]
+        self.aws = torch.empty(mu.adamw_workspace_size(h, self.ts), dtype=torch.uint8, device=DEV)
+        self.norm = torch.zeros(1, device=DEV)
+        self.ahp = mu.adamw_hparams(step=3, **synth.ADAMW_DEFAULT)
+
+    def __call__(self):
+        mu.muon_step_batched(self.h, self.mats, self.hp, self.ws)
+        mu.adamw_step_clipped(self.h, self.ts, self.ahp, 1.0, self.aws, norm_out=self.norm)
+
+
+def test_graph_replays_equal_eager_steps():
+    h = Handle.get()
+    eager_state, graph_state = _state(11), _state(11)
+    eager, captured = Step(h, eager_state), Step(h, graph_state)
+    torch.cuda.synchronize()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        captured()
+    torch.cuda.synchronize()
+    # capturing runs nothing
+    for a, b in zip(graph_state["W"], eager_state["W"]):
+        assert torch.equal(a, b)
+
+    for r in range(4):
+        graph.replay()
+        eager()
+        torch.cuda.synchronize()
+        for key in ("W", "M", "P", "m", "v"):
+            for i, (a, b) in enumerate(zip(graph_state[key], eager_state[key])):
+                assert torch.equal(a, b), (r, key, i)
+        assert torch.equal(captured.norm, eager.norm), r
+        assert float(eager.norm) > 1.0  # the clip was active
+        # eager work between replays: new gradients in the buffers the graph reads
+        for a, b in zip(graph_state["G"], eager_state["G"]):
+            a.mul_(-0.75).add_(0.01)
+            b.mul_(-0.75).add_(0.01)
+        torch.cuda.synchronize()
