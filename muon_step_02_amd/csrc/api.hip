@@ -227,8 +227,11 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         d.cols_pad = (int32_t)pad_to(m.cols, pad);
         d.mp = d.transposed ? d.cols_pad : d.rows_pad;
         d.np = d.transposed ? d.rows_pad : d.cols_pad;
-        d.ew_tiles_c = d.cols_pad / kEwTile;
-        d.ew_tiles = (d.rows_pad / kEwTile) * d.ew_tiles_c;
+        // 16 x 256 streaming tiles unless Y is also needed transposed (the
+        // fp32 iteration keeps X^T; bf16 writes Y^T when rows > cols)
+        d.ew_th = (!P.ns_f32 && !d.transposed && d.cols_pad % 256 == 0) ? 16 : kEwTile;
+        d.ew_tiles_c = d.cols_pad / (4096 / d.ew_th);
+        d.ew_tiles = (d.rows_pad / d.ew_th) * d.ew_tiles_c;
         d.vec4 = need_ptrs && m.cols % 4 == 0 &&
                  aligned_rows(m.param, m.ld_param, elem_bytes(m.param_dtype)) &&
                  aligned_rows(m.grad, m.ld_grad, elem_bytes(m.grad_dtype)) &&

@@ -149,14 +149,28 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return t;
 }
 
-template <bool VEC, bool NS_F32>
+// Elementwise tiles hold 4096 elements: TH x (4096 / TH).  Square 64 x 64
+// tiles go through LDS when Y is also needed transposed; 16 x 256 tiles
+// (matrices whose bf16 iteration input is Y itself) give every wave
+// instruction one contiguous 1 KB (fp32) row segment.  256 threads, each four
+// columns of four rows (rr + RPP q).
+template <int TH>
+struct EwTile {
+    static constexpr int TW = 4096 / TH;
+    static constexpr int TPR = TW / 4;    // threads per row
+    static constexpr int RPP = 256 / TPR; // rows per pass
+    static_assert(RPP * 4 == TH, "four passes cover the tile");
+};
+
+template <bool VEC, bool NS_F32, int TH>
 __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu, int nesterov,
                                               float (*tileT)[kEwTile + 1], float* red) {
+    using T = EwTile<TH>;
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
-    const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
+    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * T::TW;
     const int t = threadIdx.x;
-    const int cg = (t & 15) * 4;
-    const int rr = t >> 4;
+    const int cg = (t % T::TPR) * 4;
+    const int rr = t / T::TPR;
     const int64_t rows = d.rows, cols = d.cols;
     const int gbf = d.grad_dtype == MUON_BF16;
     // natural orientation (rows_pad x cols_pad, ld cols_pad) and transposed
@@ -166,7 +180,7 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     void* nat = d.transposed ? d.xt[0] : d.x[0];
     void* trn = d.transposed ? d.x[0] : d.xt[0];
     const bool write_nat = NS_F32 || !d.transposed;
-    const bool write_trn = NS_F32 || d.transposed;
+    const bool write_trn = TH == kEwTile && (NS_F32 || d.transposed);
     const int64_t ld_nat = d.cols_pad, ld_trn = d.rows_pad;
     const float omm = 1.f - mu;
     float ss = 0.f;
@@ -175,7 +189,7 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     int valid[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int64_t r = r0 + rr + 16 * q;
+        const int64_t r = r0 + rr + T::RPP * q;
         const int64_t cv = cols - (c0 + cg);
         valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
         if (valid[q] > 0) {
@@ -185,7 +199,7 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int lr = rr + 16 * q;
+        const int lr = rr + T::RPP * q;
         const int64_t r = r0 + lr;
         const int64_t c = c0 + cg;
         float y[4] = {0.f, 0.f, 0.f, 0.f};
@@ -201,8 +215,10 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
             store4<VEC>(d.mom, 0, r * d.ld_mom + c, m[q], valid[q]);
         }
         if (write_nat) store_ns4<NS_F32>(nat, r * ld_nat + c, y);
+        if (TH == kEwTile) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tileT[cg + e][lr] = y[e];
+            for (int e = 0; e < 4; ++e) tileT[cg + e][lr] = y[e];
+        }
     }
     if (write_trn) {
         __syncthreads();
@@ -229,10 +245,17 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
-    if (d.vec4)
-        momentum_tile<true, NS_F32>(d, lt, mu, nesterov, tileT, red);
-    else
-        momentum_tile<false, NS_F32>(d, lt, mu, nesterov, tileT, red);
+    if (d.ew_th == 16) {
+        if (d.vec4)
+            momentum_tile<true, NS_F32, 16>(d, lt, mu, nesterov, tileT, red);
+        else
+            momentum_tile<false, NS_F32, 16>(d, lt, mu, nesterov, tileT, red);
+    } else {
+        if (d.vec4)
+            momentum_tile<true, NS_F32, kEwTile>(d, lt, mu, nesterov, tileT, red);
+        else
+            momentum_tile<false, NS_F32, kEwTile>(d, lt, mu, nesterov, tileT, red);
+    }
 }
 
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
@@ -254,20 +277,21 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
     }
 }
 
-template <bool VEC, bool NS_F32>
+template <bool VEC, bool NS_F32, int TH>
 __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity, float decay,
                                            float step, float qk_tau, float (*tileT)[kEwTile + 1]) {
+    using T = EwTile<TH>;
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
-    const int64_t r0 = (int64_t)tr * kEwTile, c0 = (int64_t)tc * kEwTile;
+    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * T::TW;
     const int t = threadIdx.x;
-    const int cg = (t & 15) * 4;
-    const int rr = t >> 4;
+    const int cg = (t % T::TPR) * 4;
+    const int rr = t / T::TPR;
     const int64_t rows = d.rows, cols = d.cols;
     const int pbf = d.param_dtype == MUON_BF16;
     // O in the weight's orientation (rows_pad x cols_pad, ld cols_pad): X
     // when not transposed, else X^T, which the fp32 iteration keeps and the
     // bf16 one gets by transposing X (cols_pad x rows_pad) through LDS.
-    const bool via_lds = !NS_F32 && d.transposed;
+    const bool via_lds = TH == kEwTile && !NS_F32 && d.transposed;
     const void* O = d.transposed ? (NS_F32 ? d.xt[parity] : d.x[parity]) : d.x[parity];
     const int64_t ld_o = d.cols_pad;
     const float sc = step * d.scale;
@@ -289,7 +313,7 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int64_t r = r0 + rr + 16 * q;
+        const int64_t r = r0 + rr + T::RPP * q;
         const int64_t cv = cols - (c0 + cg);
         valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
         if (valid[q] > 0) {
@@ -305,7 +329,7 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (valid[q] == 0) continue;
-        const int64_t r = r0 + rr + 16 * q;
+        const int64_t r = r0 + rr + T::RPP * q;
         const int64_t c = c0 + cg;
         // QK-Clip: rows of head h scaled by sqrt(tau / S_max^h) when S_max^h > tau
         float clip = 1.f;
@@ -335,10 +359,17 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
-    if (d.vec4)
-        apply_tile<true, NS_F32>(d, lt, parity, decay, step, qk_tau, tileT);
-    else
-        apply_tile<false, NS_F32>(d, lt, parity, decay, step, qk_tau, tileT);
+    if (d.ew_th == 16) {
+        if (d.vec4)
+            apply_tile<true, NS_F32, 16>(d, lt, parity, decay, step, qk_tau, tileT);
+        else
+            apply_tile<false, NS_F32, 16>(d, lt, parity, decay, step, qk_tau, tileT);
+    } else {
+        if (d.vec4)
+            apply_tile<true, NS_F32, kEwTile>(d, lt, parity, decay, step, qk_tau, tileT);
+        else
+            apply_tile<false, NS_F32, kEwTile>(d, lt, parity, decay, step, qk_tau, tileT);
+    }
 }
 
 // ------------------------------------------------------ table upload ----

@@ -43,7 +43,8 @@ __device__ __forceinline__ void gst(T* p, const T& v) {
 constexpr int kPadBf16 = 256;
 constexpr int kSmallBf16 = 128;
 constexpr int kPadF32 = 64;
-// Elementwise kernels (momentum, apply) work on 64 x 64 tiles of the weight.
+// Elementwise kernels (momentum, apply) work on tiles of 4096 elements of the
+// weight: 64 x 64 where Y is needed transposed, else 16 x 256.
 constexpr int kEwTile = 64;
 
 // One matrix as the kernels see it.  Built on the host, copied into the
@@ -63,6 +64,7 @@ struct MatDesc {
     int32_t transposed;  // rows > cols: the iteration runs on W^T
     int32_t mp, np;      // padded canonical dims: m' = min, n' = max
     int32_t rows_pad, cols_pad;
+    int32_t ew_th;       // elementwise tile height: kEwTile (square) or 16 (16 x 256)
     int32_t ew_tiles_c;  // elementwise tiles along cols_pad
     int32_t ew_tiles;    // elementwise tiles of this matrix
     int32_t vec4;        // 1: every row start of param/grad/mom is 16B aligned and cols % 4 == 0
