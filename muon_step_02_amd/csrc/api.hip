@@ -2,7 +2,7 @@
 // launch sequence of one Muon step; the AdamW entry point.
 //
 // One call of muon_step_batched enqueues, on the caller's stream:
-//   1 async copy of the descriptor table (pinned host slot -> workspace),
+//   the descriptor-table upload (kernel arguments -> workspace, 2 KB a launch),
 //   momentum (all matrices), norm finalize (all matrices),
 //   ns_steps x {gram, poly, update} (each one grouped launch over all matrices),
 //   apply (all matrices).

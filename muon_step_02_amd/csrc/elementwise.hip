@@ -1,11 +1,14 @@
 // Memory-bound kernels of the Muon step and the AdamW fallback (gfx950).
 //
 //   momentum_kernel  M <- mu M + (1-mu) G; Y <- Nesterov blend; per-tile
-//                    sum of Y^2; Y written (unnormalised) in both the
-//                    natural and the transposed orientation of the padded
-//                    Newton-Schulz buffers, with zeros in the padding.
+//                    sum of Y^2; Y written (unnormalised) into the padded
+//                    Newton-Schulz buffer in the canonical orientation (Y or,
+//                    for rows > cols, Y^T through LDS; the fp32 iteration
+//                    keeps both), with zeros in the padding.
 //   norm_finalize    ||Y||_F from the per-tile partial sums (fixed order, so
 //                    every run gives the same bits) and s = 1/(||Y||_F + eps).
+//   table_upload     the host-built descriptor table, carried in kernel
+//                    arguments.
 //   apply_kernel     W <- (1 - lr wd) W - lr scale O, then the optional
 //                    QK-Clip row scaling ("The Optimizer Wars ...", section
 //                    "What is MuonClip?").

@@ -510,9 +510,9 @@ __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
     tj = lt - t * (t + 1) / 2;
 }
 
-// Update tiles in groups of GRP tile-rows: within a group the column index
-// advances slowest, so concurrently running tiles reuse a few B row-slabs and
-// X^T row-slabs.
+// Update tiles in groups of kUpdGroup tile-rows: within a group the column
+// index advances slowest, so concurrently running tiles reuse a few B
+// row-panels and X column-panels.
 constexpr int kUpdGroup = 8;
 __device__ __forceinline__ void grouped_index(int lt, int trows, int tcols, int& ti, int& tj) {
     const int g = lt / (kUpdGroup * tcols);

@@ -37,8 +37,9 @@ __device__ __forceinline__ void gst(T* p, const T& v) {
 
 // Canonical Newton-Schulz buffers are padded to these multiples so the GEMM
 // kernels run on whole tiles with no bounds checks.  The padding is zero and
-// the iteration keeps it zero: rows/cols of zeros stay zero under X X^T,
-// b A + c A A and a X + B X.  bf16 matrices whose short side is at most
+// the iteration keeps it zero: zero rows/cols of X give zero rows/cols of
+// A = X X^T, B = a I + b A + c A A is a I on the padded block, and B X maps
+// the zero padded rows of X to zero.  bf16 matrices whose short side is at most
 // kSmallBf16 use 128-wide tiles and padding ("small" class), the others 256.
 constexpr int kPadBf16 = 256;
 constexpr int kSmallBf16 = 128;
