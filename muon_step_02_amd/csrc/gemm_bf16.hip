@@ -27,7 +27,7 @@
 // Tiling: a workgroup computes a BM x BN tile with WM x WN waves, each wave a
 // (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16,
 // fp32 accumulation).  K advances in slabs of 64: operand slabs are copied
-// global->LDS with global_load_lds_dwordx4 (16 bytes per lane, no VGPR
+// global->LDS with buffer_load_dwordx4 ... lds (16 bytes per lane, no VGPR
 // staging) into LDS stages (two for 256 x 256 tiles, four for 128 x 128), so
 // the copies of later slabs overlap the MFMAs on slab k.  The epilogue goes
 // through LDS so that every global access is a coalesced 16-byte one.  LDS
@@ -50,6 +50,13 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Raw buffer resource over `base` (gfx9 family: 32-bit data format, no
+// stride, no swizzle; offsets up to 2 GB).  A slab copy through it needs one
+// 32-bit offset register per lane instead of a 64-bit address.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, 0x7fffffff, 0x00020000);
+}
+
 enum { GRAM = 0, POLY = 1, UPDATE = 2 };
 
 // LDS is four 32 KB arrays (see Stages).
@@ -65,7 +72,7 @@ struct Cfg {
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 32, FN = TN / 32;
     static constexpr int CH = BK / 8;          // 16-byte chunks per LDS row
-    static constexpr int RPI = 64 / CH;        // rows per global_load_lds (1 KB)
+    static constexpr int RPI = 64 / CH;        // rows per 1 KB slab copy
     static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
     static constexpr int LPS = ((BM + BN) / RPI) / NW;  // slab copies per stage per wave
     // a stage is one LDS array (P slab, then Q slab) or, when each slab fills
@@ -129,22 +136,23 @@ __device__ __forceinline__ int swz(int row) {
 
 // Copy rows [0, R) x k-chunk [0, BK) of a row-major bf16 operand (rows start
 // at `g`, leading dimension ld) into an LDS slab, swizzled.  One
-// global_load_lds_dwordx4 moves 1 KB (RPI rows, contiguous in LDS); lane L
+// buffer_load_dwordx4 ... lds moves 1 KB (RPI rows, contiguous in LDS); lane L
 // fills chunk position L % CH of row L / CH, i.e. it fetches logical chunk
 // (L % CH) ^ swz(row).
 template <class C, int R>
 __device__ __forceinline__ void load_slab(const uint16_t* __restrict__ g, int64_t ld, uint16_t* slab,
                                           int wave, int lane) {
     constexpr int PER_WAVE = (R / C::RPI) / C::NW;
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc(g);
     const int lrow = lane / C::CH;
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
         const int grp = wave * PER_WAVE + q;
         const int row = grp * C::RPI + lrow;
         const int lch = (lane % C::CH) ^ swz<C::BK>(row);
-        const uint16_t* src = g + (int64_t)row * ld + lch * 8;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * C::RPI * C::BK),
-                                         16, 0, 0);
+        const uint32_t off = (uint32_t)(row * (int)ld + lch * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slab + grp * C::RPI * C::BK), 16,
+                                                 off, 0, 0, 0);
     }
 }
 
@@ -162,7 +170,7 @@ __device__ __forceinline__ bf16x8 read_frag(const uint16_t* slab, int row, int l
 __device__ __forceinline__ int swzk(int k) { return (k & 3) << 2; }
 
 // Copy rows [0, BK) (k) x columns [0, BN) of a row-major bf16 matrix (row k
-// at g + k * ld) into a k-major slab.  One global_load_lds_dwordx4 moves 1 KB
+// at g + k * ld) into a k-major slab.  One buffer_load_dwordx4 ... lds moves 1 KB
 // = 1024 / (2 BN) rows; lane L fills chunk position L % CQ of row L / CQ.
 template <class C>
 __device__ __forceinline__ void load_slab_kn(const uint16_t* __restrict__ g, int64_t ld,
@@ -171,15 +179,16 @@ __device__ __forceinline__ void load_slab_kn(const uint16_t* __restrict__ g, int
     constexpr int RPK = 64 / CQ;           // rows per copy
     constexpr int PER_WAVE = (C::BK / RPK) / C::NW;
     static_assert((C::BK / RPK) % C::NW == 0, "k-major slab rows must split over waves");
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc(g);
     const int lrow = lane / CQ;
     const int p = lane % CQ;
 #pragma unroll
     for (int q = 0; q < PER_WAVE; ++q) {
         const int grp = wave * PER_WAVE + q;
         const int k = grp * RPK + lrow;
-        const uint16_t* src = g + (int64_t)k * ld + (p ^ swzk(k)) * 8;
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(slab + grp * RPK * C::BN),
-                                         16, 0, 0);
+        const uint32_t off = (uint32_t)(k * (int)ld + (p ^ swzk(k)) * 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slab + grp * RPK * C::BN), 16, off,
+                                                 0, 0, 0);
     }
 }
 

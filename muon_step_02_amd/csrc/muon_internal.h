@@ -94,7 +94,9 @@ __device__ __forceinline__ int find_matrix(const int32_t* prefix, int n, int32_t
         int mid = (lo + hi + 1) >> 1;
         if (gld(prefix + mid) <= tile) lo = mid; else hi = mid - 1;
     }
-    return lo;
+    // uniform across the workgroup: descriptor fields then come through
+    // scalar loads into scalar registers
+    return __builtin_amdgcn_readfirstlane(lo);
 }
 
 // ---- bf16 helpers (round to nearest even, as a hardware conversion) -------
