@@ -406,6 +406,39 @@ __device__ __forceinline__ int adamw_tensor_of(const AdamwGroup& grp, int blk) {
     return lo;
 }
 
+// One whole chunk on the vector path.  Every load of the chunk is issued
+// before the first store: the compiler cannot move a load above a store to a
+// pointer it may alias, so a load/compute/store loop would keep only one
+// quarter of the chunk in flight per thread.
+template <bool PBF, bool GBF>
+__device__ __forceinline__ void adamw_chunk_vec(void* P, const void* G, float* M, float* V,
+                                                int64_t start, float gs, float lr, float b1,
+                                                float b2, float eps, float wd, float inv_bc1,
+                                                float inv_bc2) {
+    constexpr int Q = kAdamwChunk / 1024;
+    Vals4 th[Q], g[Q];
+    float4 m[Q], v[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int64_t off = start + q * 1024 + threadIdx.x * 4;
+        th[q] = load4<true>(P, PBF, off, 4);
+        g[q] = load4<true>(G, GBF, off, 4);
+        m[q] = ld_nt(M + off);
+        v[q] = ld_nt(V + off);
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int64_t off = start + q * 1024 + threadIdx.x * 4;
+        adamw_elem(th[q].v[0], gs * g[q].v[0], m[q].x, v[q].x, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+        adamw_elem(th[q].v[1], gs * g[q].v[1], m[q].y, v[q].y, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+        adamw_elem(th[q].v[2], gs * g[q].v[2], m[q].z, v[q].z, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+        adamw_elem(th[q].v[3], gs * g[q].v[3], m[q].w, v[q].w, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+        store4<true>(P, PBF, off, th[q], 4);
+        st_nt(M + off, m[q]);
+        st_nt(V + off, v[q]);
+    }
+}
+
 // gscale: null, or a device scalar every gradient is multiplied by first
 // (global-norm clipping).
 __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, float b1, float b2,
@@ -423,22 +456,17 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
     float* V = grp.v[ti];
     const int pbf = grp.param_bf16[ti], gbf = grp.grad_bf16[ti];
     if (grp.vec4[ti] && end - start == kAdamwChunk) {
-#pragma unroll
-        for (int q = 0; q < kAdamwChunk / 1024; ++q) {
-            const int64_t off = start + q * 1024 + threadIdx.x * 4;
-            Vals4 th = load4<true>(P, pbf, off, 4);
-            Vals4 g = load4<true>(G, gbf, off, 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) g.v[e] *= gs;
-            float4 m = ld_nt(M + off);
-            float4 v = ld_nt(V + off);
-            adamw_elem(th.v[0], g.v[0], m.x, v.x, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
-            adamw_elem(th.v[1], g.v[1], m.y, v.y, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
-            adamw_elem(th.v[2], g.v[2], m.z, v.z, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
-            adamw_elem(th.v[3], g.v[3], m.w, v.w, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
-            store4<true>(P, pbf, off, th, 4);
-            st_nt(M + off, m);
-            st_nt(V + off, v);
+        // the dtypes are uniform over the workgroup: branch once, outside the chunk
+        if (pbf) {
+            if (gbf)
+                adamw_chunk_vec<true, true>(P, G, M, V, start, gs, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            else
+                adamw_chunk_vec<true, false>(P, G, M, V, start, gs, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+        } else {
+            if (gbf)
+                adamw_chunk_vec<false, true>(P, G, M, V, start, gs, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
+            else
+                adamw_chunk_vec<false, false>(P, G, M, V, start, gs, lr, b1, b2, eps, wd, inv_bc1, inv_bc2);
         }
     } else {
         for (int64_t i = start + threadIdx.x; i < end; i += 256) {
@@ -459,7 +487,10 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamwGroup grp, float lr, fl
 }
 
 // Sum of squares of the gradients of one group, one partial per block of
-// kAdamwChunk elements, written at partials[block_offset + block].
+// kAdamwChunk elements, written at partials[block_offset + block].  Every
+// thread issues its four loads before the first product.  (Two or more
+// chunks per workgroup, with all of their loads issued at once, measured
+// slower: the many small workgroups keep more of the chip busy.)
 __global__ __launch_bounds__(256) void adamw_sumsq_kernel(AdamwGroup grp, float* partials,
                                                           int block_offset) {
     __shared__ float red[4];
@@ -471,10 +502,26 @@ __global__ __launch_bounds__(256) void adamw_sumsq_kernel(AdamwGroup grp, float*
     const void* G = grp.grad[ti];
     const int gbf = grp.grad_bf16[ti];
     float ss = 0.f;
-    for (int64_t i = start + threadIdx.x; i < end; i += 256) {
-        const float g = gbf ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(G) + i))
-                            : gld(reinterpret_cast<const float*>(G) + i);
-        ss += g * g;
+    if (grp.vec4[ti] && end - start == kAdamwChunk) {
+        constexpr int Q = kAdamwChunk / 1024;
+        Vals4 g[Q];
+        if (gbf) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) g[q] = load4<true>(G, 1, start + q * 1024 + threadIdx.x * 4, 4);
+        } else {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) g[q] = load4<true>(G, 0, start + q * 1024 + threadIdx.x * 4, 4);
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += g[q].v[e] * g[q].v[e];
+    } else {
+        for (int64_t i = start + threadIdx.x; i < end; i += 256) {
+            const float g = gbf ? bf16_bits_to_f32(gld(reinterpret_cast<const uint16_t*>(G) + i))
+                                : gld(reinterpret_cast<const float*>(G) + i);
+            ss += g * g;
+        }
     }
     const float tot = block_sum_256(ss, red);
     if (threadIdx.x == 0) gst(partials + block_offset + blk, tot);

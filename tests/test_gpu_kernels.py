@@ -311,7 +311,7 @@ ADAMW_HP = dict(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 
 @pytest.mark.parametrize("pdt,gdt", [(torch.float32, torch.float32), (torch.float32, torch.bfloat16),
-                                     (torch.bfloat16, torch.bfloat16)])
+                                     (torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16)])
 def test_adamw_many_tensors_three_steps(pdt, gdt):
     h = Handle.get()
     sizes = [1, 3, 4095, 4096, 4097, 10000, 65539, 0] + [257 * k for k in range(1, 33)]

@@ -136,8 +136,9 @@ def test_three_step_schedule_and_per_iteration_coefficients_bf16():
 ADAMW_HP = dict(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 
-@pytest.mark.parametrize("scale", [1.0, 1e-4])
-def test_adamw_global_norm_clipping(scale):
+@pytest.mark.parametrize("scale,gdt", [(1.0, torch.float32), (1e-4, torch.float32),
+                                       (1.0, torch.bfloat16)])
+def test_adamw_global_norm_clipping(scale, gdt):
     h = Handle.get()
     g = torch.Generator(device=DEV).manual_seed(21)
     sizes = [3, 4096, 70000, 1024 * 1024 + 5] + [999] * 35
@@ -148,7 +149,7 @@ def test_adamw_global_norm_clipping(scale):
     norm_out = torch.zeros(1, device=DEV)
     ws = None
     for t in range(1, 4):
-        grads = [torch.randn(n, generator=g, device=DEV) * scale for n in sizes]
+        grads = [(torch.randn(n, generator=g, device=DEV) * scale).to(gdt) for n in sizes]
         ts = [mu.adamw_tensor(p, gr, m, v) for p, gr, m, v in zip(P, grads, Ms, Vs)]
         if ws is None:
             ws = torch.empty(mu.adamw_workspace_size(h, ts), dtype=torch.uint8, device=DEV)
