@@ -85,6 +85,7 @@ struct Cfg {
                   "a stage is one array, or one array per operand");
     static_assert(NARR <= 4, "four LDS arrays");
     static_assert(RB * BN * 4 <= kLdsArr * 2, "epilogue band must fit one array");
+    static_assert(BN % 64 == 0, "the band swizzle permutes columns within runs of 64");
     static_assert(BK == 32 || BK == 64, "BK is 32 or 64");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 MFMA tile");
@@ -115,12 +116,14 @@ __device__ __forceinline__ uint16_t* stage_q(const Stages& st, int i) {
 }
 
 // Epilogue band buffer (fp32, RB x BN, in array 0), unpadded: column c of row
-// r sits at c ^ ((r & 4) << 3), so the two half-waves of an accumulator store
-// (rows r and r + 4) land 32 banks apart, and runs of 8 columns stay
-// contiguous.
+// r sits at c ^ ((r & 4) << 3) ^ ((r >> 3) << 4).  The first term puts the two
+// half-waves of an accumulator store (rows r and r + 4) 32 banks apart; the
+// second puts the four rows r, r + 8, r + 16, r + 24 that one instruction of
+// the transposed pass reads for each column 16 banks apart.  Both leave runs
+// of 16 columns contiguous.
 template <class C>
 __device__ __forceinline__ int sbi(int r, int c) {
-    return r * C::BN + (c ^ ((r & 4) << 3));
+    return r * C::BN + (c ^ ((r & 4) << 3) ^ ((r >> 3) << 4));
 }
 
 // LDS slab layout: row r holds BK bf16 = CH chunks of 16 bytes; logical chunk
