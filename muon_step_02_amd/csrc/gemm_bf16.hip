@@ -215,6 +215,16 @@ __device__ __forceinline__ bf16x8 read_frag_kn(const uint16_t* slab, int k0, int
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Output stores of the epilogue: streaming (nt) and at device scope (sc1), so
+// they are written through L2 without displacing the operand slabs that the
+// other tiles of the XCD are still reading.  `base` is uniform (a row band or
+// a column band of the output); the byte offset stays far below 2 GB.
+constexpr int kStreamStore = 2 | 16;  // cache policy bits: nt | sc1
+__device__ __forceinline__ void store_out(uint16_t* base, uint32_t byte_off, const uint4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(GWord<16>::T, v), slab_rsrc(base),
+                                           byte_off, 0, kStreamStore);
+}
+
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
@@ -453,7 +463,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
             o.y = pack2(v[2], v[3]);
             o.z = pack2(v[4], v[5]);
             o.w = pack2(v[6], v[7]);
-            gst(reinterpret_cast<uint4*>(ep.out + (brow + rr) * ep.ld_out + col0 + c8), o);
+            store_out(ep.out + brow * ep.ld_out + col0, (uint32_t)(rr * ep.ld_out + c8) * 2u, o);
             if (ep.outT) {
                 *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
@@ -473,7 +483,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                 o.y = pack2(v[2], v[3]);
                 o.z = pack2(v[4], v[5]);
                 o.w = pack2(v[6], v[7]);
-                gst(reinterpret_cast<uint4*>(ep.outT + (col0 + c) * ep.ld_outT + brow + i8), o);
+                store_out(ep.outT + col0 * ep.ld_outT + brow, (uint32_t)(c * ep.ld_outT + i8) * 2u, o);
             }
         }
         if (HAS_E) {
