@@ -103,6 +103,9 @@ muon_status check_hparams(const muon_hparams* hp) {
 }
 
 constexpr int64_t kMaxDim = 1 << 20;
+static_assert(kSmallBf16 % kTrTH == 0 && kSmallBf16 % kTrTW == 0,
+              "transposing elementwise tiles must divide every bf16 padding");
+static_assert(kPadF32 % kEwTile == 0, "fp32 elementwise tiles must divide the fp32 padding");
 
 muon_status check_matrix(const muon_matrix& m, bool need_ptrs) {
     if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return MUON_ERR_INVALID_ARG;
@@ -150,11 +153,12 @@ struct ClassPlan {
 
 struct Plan {
     std::vector<MatDesc> d;
-    std::vector<int32_t> pew;
+    std::vector<int32_t> pew;        // elementwise tiles of all kinds (norm partial offsets)
+    std::vector<int32_t> pek[2];     // elementwise tiles by kind (launch prefixes)
     ClassPlan cls[2];  // 0 large, 1 small
-    size_t off_pew = 0, table_bytes = 0;
+    size_t off_pek[2] = {0, 0}, table_bytes = 0;
     size_t off_partials = 0, off_invnorm = 0, total = 0;
-    int total_ew = 0;
+    int total_ek[2] = {0, 0};
     int ns_f32 = 0;
 };
 
@@ -188,7 +192,9 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
 
     P.d.assign(n, MatDesc{});
     P.pew.assign(n + 1, 0);
-    int64_t tew = 0;
+    P.pek[0].assign(n + 1, 0);
+    P.pek[1].assign(n + 1, 0);
+    int64_t tew = 0, tek[2] = {0, 0};
     int nsmall = 0;
     for (int i = 0; i < n; ++i) nsmall += is_small(i) ? 1 : 0;
     P.cls[0].first = 0;
@@ -229,8 +235,16 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         d.np = d.transposed ? d.rows_pad : d.cols_pad;
         // 16 x 256 streaming tiles unless Y is also needed transposed (the
         // fp32 iteration keeps X^T; bf16 writes Y^T when rows > cols)
-        d.ew_th = (!P.ns_f32 && !d.transposed && d.cols_pad % 256 == 0) ? 16 : kEwTile;
-        d.ew_tiles_c = d.cols_pad / (4096 / d.ew_th);
+        if (P.ns_f32) {
+            d.ew_th = d.ew_tw = kEwTile;
+        } else if (!d.transposed && d.cols_pad % 256 == 0) {
+            d.ew_th = 16;
+            d.ew_tw = 256;
+        } else {
+            d.ew_th = kTrTH;
+            d.ew_tw = kTrTW;
+        }
+        d.ew_tiles_c = d.cols_pad / d.ew_tw;
         d.ew_tiles = (d.rows_pad / d.ew_th) * d.ew_tiles_c;
         d.vec4 = need_ptrs && m.cols % 4 == 0 &&
                  aligned_rows(m.param, m.ld_param, elem_bytes(m.param_dtype)) &&
@@ -241,16 +255,20 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         const int64_t gram_tiles = P.ns_f32 ? Ts * Ts : Ts * (Ts + 1) / 2;
         const int64_t upd_tiles = (d.mp / updM) * (d.np / updN);
         tew += d.ew_tiles;
+        tek[d.ew_th == 16 ? 0 : 1] += d.ew_tiles;
         tgram[c] += gram_tiles;
         tupd[c] += upd_tiles;
         if (tew > INT32_MAX || tgram[c] > INT32_MAX / 2 || tupd[c] > INT32_MAX / 2)
             return MUON_ERR_INVALID_ARG;
         P.pew[k + 1] = (int32_t)tew;
+        P.pek[0][k + 1] = (int32_t)tek[0];
+        P.pek[1][k + 1] = (int32_t)tek[1];
         const int kc = k - P.cls[c].first;
         P.cls[c].pgram[kc + 1] = (int32_t)tgram[c];
         P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
     }
-    P.total_ew = (int)tew;
+    P.total_ek[0] = (int)tek[0];
+    P.total_ek[1] = (int)tek[1];
     for (int c = 0; c < 2; ++c) {
         ClassPlan& C = P.cls[c];
         C.total_gram = (int)tgram[c];
@@ -273,8 +291,10 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
     }
 
     size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
-    P.off_pew = off;
-    off = align_up(off + (size_t)(n + 1) * 4, 256);
+    for (int kind = 0; kind < 2; ++kind) {
+        P.off_pek[kind] = off;
+        off = align_up(off + (size_t)(n + 1) * 4, 256);
+    }
     for (int c = 0; c < 2; ++c) {
         P.cls[c].off_pgram = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
@@ -416,7 +436,8 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     h->table.assign(P.table_bytes, 0);
     char* hb = h->table.data();
     memcpy(hb, P.d.data(), (size_t)n * sizeof(MatDesc));
-    memcpy(hb + P.off_pew, P.pew.data(), (size_t)(n + 1) * 4);
+    for (int kind = 0; kind < 2; ++kind)
+        memcpy(hb + P.off_pek[kind], P.pek[kind].data(), (size_t)(n + 1) * 4);
     for (const ClassPlan& c : P.cls) {
         memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
@@ -424,18 +445,19 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     if (launch_table_upload(hb, P.table_bytes, workspace, s) != hipSuccess) return MUON_ERR_HIP;
 
     const MatDesc* dd = reinterpret_cast<const MatDesc*>(workspace);
-    Prefix pf;  // elementwise kernels: all matrices
-    pf.ew = reinterpret_cast<const int32_t*>(ws + P.off_pew);
-    pf.gram = pf.upd = nullptr;
+    EwGroups eg;  // elementwise kernels: all matrices, by tile kind
+    for (int kind = 0; kind < 2; ++kind) {
+        eg.prefix[kind] = reinterpret_cast<const int32_t*>(ws + P.off_pek[kind]);
+        eg.tiles[kind] = P.total_ek[kind];
+    }
     Prefix pc[2];
     for (int c = 0; c < 2; ++c) {
-        pc[c].ew = nullptr;
         pc[c].gram = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pgram);
         pc[c].upd = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pupd);
     }
 
     hipError_t e = timed(h, 0, s, [&] {
-        return launch_momentum(dd, n, pf, P.total_ew, hp->momentum, hp->nesterov, P.ns_f32, s);
+        return launch_momentum(dd, n, eg, hp->momentum, hp->nesterov, P.ns_f32, s);
     });
     if (e == hipSuccess) e = timed(h, 1, s, [&] { return launch_norm_finalize(dd, n, hp->eps, s); });
     for (int it = 0; it < hp->ns_steps && e == hipSuccess; ++it) {
@@ -476,7 +498,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     }
     if (e == hipSuccess)
         e = timed(h, 5, s, [&] {
-            return launch_apply(dd, n, pf, P.total_ew, hp->ns_steps & 1, hp->lr, hp->weight_decay,
+            return launch_apply(dd, n, eg, hp->ns_steps & 1, hp->lr, hp->weight_decay,
                                 hp->qk_tau, P.ns_f32, s);
         });
     return hip_status(e);

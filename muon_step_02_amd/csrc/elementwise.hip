@@ -152,30 +152,46 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
     return t;
 }
 
-// Elementwise tiles hold 4096 elements: TH x (4096 / TH).  Square 64 x 64
-// tiles go through LDS when Y is also needed transposed; 16 x 256 tiles
-// (matrices whose bf16 iteration input is Y itself) give every wave
-// instruction one contiguous 1 KB (fp32) row segment.  256 threads, each four
-// columns of four rows (rr + RPP q).
-template <int TH>
+// Elementwise tiles: TH x TW elements of the weight, 256 threads, each four
+// consecutive columns of NP rows (rr + RPP q).  Three shapes:
+//  - 16 x 256 streaming tiles where the bf16 iteration input is Y itself:
+//    every wave instruction is one contiguous 1 KB (fp32) row segment;
+//  - kTrTH x kTrTW tiles where the bf16 iteration runs on Y^T (rows > cols):
+//    the tile goes through LDS; momentum stores Y transposed, apply reads X
+//    transposed.  The tile is wide so the fp32 row segments are 512 B long;
+//    that matters more than the length of the transposed bf16 rows (TH);
+//  - 64 x 64 tiles for the fp32 iteration, which keeps both Y and Y^T.
+template <int TH_, int TW_>
 struct EwTile {
-    static constexpr int TW = 4096 / TH;
-    static constexpr int TPR = TW / 4;    // threads per row
-    static constexpr int RPP = 256 / TPR; // rows per pass
-    static_assert(RPP * 4 == TH, "four passes cover the tile");
+    static constexpr int TH = TH_, TW = TW_;
+    static constexpr int TPR = TW / 4;     // threads per row
+    static constexpr int RPP = 256 / TPR;  // rows per pass
+    static constexpr int NP = TH / RPP;    // passes
+    // the transposed tile (TW x TH), four consecutive entries per thread
+    static constexpr int TPRT = TH / 4;
+    static constexpr int RPPT = 256 / TPRT;
+    static constexpr int NPT = TW / RPPT;
+    static_assert(TPR * RPP == 256 && RPP * NP == TH, "passes cover the tile");
+    static_assert(TPRT * RPPT == 256 && RPPT * NPT == TW, "transposed passes cover the tile");
 };
 
-template <bool VEC, bool NS_F32, int TH>
+// LDS tile for the transposing shapes: TW rows of TH + 1 floats (the +1 keeps
+// both the column writes and the row reads on distinct banks).
+constexpr int lds_tile(int th, int tw) { return tw * (th + 1); }
+constexpr int kLdsT = lds_tile(kTrTH, kTrTW) > lds_tile(kEwTile, kEwTile)
+                          ? lds_tile(kTrTH, kTrTW) : lds_tile(kEwTile, kEwTile);
+
+template <bool VEC, bool NS_F32, int TH, int TW, bool GBF>
 __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu, int nesterov,
-                                              float (*tileT)[kEwTile + 1], float* red) {
-    using T = EwTile<TH>;
+                                              float* tileT, float* red) {
+    using T = EwTile<TH, TW>;
+    constexpr bool TRN = TH != 16;  // the tile goes through LDS
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
-    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * T::TW;
+    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * TW;
     const int t = threadIdx.x;
     const int cg = (t % T::TPR) * 4;
     const int rr = t / T::TPR;
     const int64_t rows = d.rows, cols = d.cols;
-    const int gbf = d.grad_dtype == MUON_BF16;
     // natural orientation (rows_pad x cols_pad, ld cols_pad) and transposed
     // orientation (cols_pad x rows_pad, ld rows_pad) of Y.  The fp32
     // iteration keeps both X and X^T; the bf16 one only the canonical X
@@ -183,25 +199,25 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
     void* nat = d.transposed ? d.xt[0] : d.x[0];
     void* trn = d.transposed ? d.x[0] : d.xt[0];
     const bool write_nat = NS_F32 || !d.transposed;
-    const bool write_trn = TH == kEwTile && (NS_F32 || d.transposed);
+    const bool write_trn = TRN && (NS_F32 || d.transposed);
     const int64_t ld_nat = d.cols_pad, ld_trn = d.rows_pad;
     const float omm = 1.f - mu;
     float ss = 0.f;
-    // all loads of the thread's four rows first, so they are in flight together
-    Vals4 g[4], m[4];
-    int valid[4];
+    // all loads of the thread's rows first, so they are in flight together
+    Vals4 g[T::NP], m[T::NP];
+    int valid[T::NP];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < T::NP; ++q) {
         const int64_t r = r0 + rr + T::RPP * q;
         const int64_t cv = cols - (c0 + cg);
         valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
         if (valid[q] > 0) {
-            g[q] = load4<VEC>(d.grad, gbf, r * d.ld_grad + c0 + cg, valid[q]);
+            g[q] = load4<VEC>(d.grad, GBF, r * d.ld_grad + c0 + cg, valid[q]);
             m[q] = load4<VEC>(d.mom, 0, r * d.ld_mom + c0 + cg, valid[q]);
         }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < T::NP; ++q) {
         const int lr = rr + T::RPP * q;
         const int64_t r = r0 + lr;
         const int64_t c = c0 + cg;
@@ -218,47 +234,66 @@ __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu
             store4<VEC>(d.mom, 0, r * d.ld_mom + c, m[q], valid[q]);
         }
         if (write_nat) store_ns4<NS_F32>(nat, r * ld_nat + c, y);
-        if (TH == kEwTile) {
+        if (TRN) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tileT[cg + e][lr] = y[e];
+            for (int e = 0; e < 4; ++e) tileT[(cg + e) * (TH + 1) + lr] = y[e];
         }
     }
     if (write_trn) {
         __syncthreads();
+        const int cgt = (t % T::TPRT) * 4;  // weight row within the tile
+        const int rrt = t / T::TPRT;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int lc = rr + 16 * q;  // column of the weight = row of Y^T
+        for (int q = 0; q < T::NPT; ++q) {
+            const int lc = rrt + T::RPPT * q;  // weight column = row of Y^T
             float v[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = tileT[lc][cg + e];
-            store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cg, v);
+            for (int e = 0; e < 4; ++e) v[e] = tileT[lc * (TH + 1) + cgt + e];
+            store_ns4<NS_F32>(trn, (c0 + lc) * ld_trn + r0 + cgt, v);
         }
     }
     const float tot = block_sum_256(ss, red);
     if (threadIdx.x == 0) gst(d.partials + lt, tot);
 }
 
-template <bool NS_F32>
+// The dtype and alignment of a matrix are uniform over the workgroup: branch
+// once here, so the tile's loads are straight-line code that can all be in
+// flight together.
+template <bool NS_F32, int TH, int TW>
+__device__ __forceinline__ void momentum_dispatch(const MatDesc& d, int lt, float mu, int nesterov,
+                                                  float* tileT, float* red) {
+    const bool gbf = d.grad_dtype == MUON_BF16;
+    if (d.vec4) {
+        if (gbf) momentum_tile<true, NS_F32, TH, TW, true>(d, lt, mu, nesterov, tileT, red);
+        else momentum_tile<true, NS_F32, TH, TW, false>(d, lt, mu, nesterov, tileT, red);
+    } else {
+        if (gbf) momentum_tile<false, NS_F32, TH, TW, true>(d, lt, mu, nesterov, tileT, red);
+        else momentum_tile<false, NS_F32, TH, TW, false>(d, lt, mu, nesterov, tileT, red);
+    }
+}
+
+// LDS: tiles of the fp32 iteration (64 x 64) or the transposing bf16 shape.
+template <bool NS_F32, bool LDS>
+constexpr int ew_lds_floats() {
+    return !LDS ? 1 : NS_F32 ? lds_tile(kEwTile, kEwTile) : lds_tile(kTrTH, kTrTW);
+}
+
+template <bool NS_F32, bool LDS>
 __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ descs, int n,
                                                        const int32_t* __restrict__ prefix,
                                                        float mu, int nesterov) {
-    __shared__ float tileT[kEwTile][kEwTile + 1];
+    __shared__ float tileT[ew_lds_floats<NS_F32, LDS>()];
     __shared__ float red[4];
     const int tile = blockIdx.x;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
-    if (d.ew_th == 16) {
-        if (d.vec4)
-            momentum_tile<true, NS_F32, 16>(d, lt, mu, nesterov, tileT, red);
-        else
-            momentum_tile<false, NS_F32, 16>(d, lt, mu, nesterov, tileT, red);
-    } else {
-        if (d.vec4)
-            momentum_tile<true, NS_F32, kEwTile>(d, lt, mu, nesterov, tileT, red);
-        else
-            momentum_tile<false, NS_F32, kEwTile>(d, lt, mu, nesterov, tileT, red);
-    }
+    if (NS_F32)
+        momentum_dispatch<true, kEwTile, kEwTile>(d, lt, mu, nesterov, tileT, red);
+    else if (!LDS)
+        momentum_dispatch<false, 16, 256>(d, lt, mu, nesterov, tileT, red);
+    else
+        momentum_dispatch<false, kTrTH, kTrTW>(d, lt, mu, nesterov, tileT, red);
 }
 
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ descs,
@@ -280,57 +315,58 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
     }
 }
 
-template <bool VEC, bool NS_F32, int TH>
+template <bool VEC, bool NS_F32, int TH, int TW, bool PBF>
 __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity, float decay,
-                                           float step, float qk_tau, float (*tileT)[kEwTile + 1]) {
-    using T = EwTile<TH>;
+                                           float step, float qk_tau, float* tileT) {
+    using T = EwTile<TH, TW>;
     const int tr = lt / d.ew_tiles_c, tc = lt - tr * d.ew_tiles_c;
-    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * T::TW;
+    const int64_t r0 = (int64_t)tr * TH, c0 = (int64_t)tc * TW;
     const int t = threadIdx.x;
     const int cg = (t % T::TPR) * 4;
     const int rr = t / T::TPR;
     const int64_t rows = d.rows, cols = d.cols;
-    const int pbf = d.param_dtype == MUON_BF16;
     // O in the weight's orientation (rows_pad x cols_pad, ld cols_pad): X
     // when not transposed, else X^T, which the fp32 iteration keeps and the
     // bf16 one gets by transposing X (cols_pad x rows_pad) through LDS.
-    const bool via_lds = TH == kEwTile && !NS_F32 && d.transposed;
+    const bool via_lds = TH != 16 && !NS_F32 && d.transposed;
     const void* O = d.transposed ? (NS_F32 ? d.xt[parity] : d.x[parity]) : d.x[parity];
     const int64_t ld_o = d.cols_pad;
     const float sc = step * d.scale;
-    float o[4][4];
-    Vals4 w[4];
-    int valid[4];
+    float o[T::NP][4];
+    Vals4 w[T::NP];
+    int valid[T::NP];
     if (via_lds) {
         // X rows c0.. (weight columns), columns r0.. (weight rows); all inside
         // the zero-padded buffer
+        const int cgt = (t % T::TPRT) * 4;
+        const int rrt = t / T::TPRT;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int lc = rr + 16 * q;
+        for (int q = 0; q < T::NPT; ++q) {
+            const int lc = rrt + T::RPPT * q;
             float v[4];
-            load_ns4<NS_F32>(O, (c0 + lc) * d.rows_pad + r0 + cg, v);
+            load_ns4<NS_F32>(O, (c0 + lc) * d.rows_pad + r0 + cgt, v);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tileT[lc][cg + e] = v[e];
+            for (int e = 0; e < 4; ++e) tileT[lc * (TH + 1) + cgt + e] = v[e];
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < T::NP; ++q) {
         const int64_t r = r0 + rr + T::RPP * q;
         const int64_t cv = cols - (c0 + cg);
         valid[q] = (r < rows && cv > 0) ? (cv >= 4 ? 4 : (int)cv) : 0;
         if (valid[q] > 0) {
             if (via_lds) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[q][e] = tileT[cg + e][rr + 16 * q];
+                for (int e = 0; e < 4; ++e) o[q][e] = tileT[(cg + e) * (TH + 1) + rr + T::RPP * q];
             } else {
                 load_ns4<NS_F32>(O, r * ld_o + c0 + cg, o[q]);
             }
-            w[q] = load4<VEC>(d.param, pbf, r * d.ld_param + c0 + cg, valid[q]);
+            w[q] = load4<VEC>(d.param, PBF, r * d.ld_param + c0 + cg, valid[q]);
         }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < T::NP; ++q) {
         if (valid[q] == 0) continue;
         const int64_t r = r0 + rr + T::RPP * q;
         const int64_t c = c0 + cg;
@@ -342,7 +378,7 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[q].v[e] = clip * (decay * w[q].v[e] - sc * o[q][e]);
-        store4<VEC>(d.param, pbf, r * d.ld_param + c, w[q], valid[q]);
+        store4<VEC>(d.param, PBF, r * d.ld_param + c, w[q], valid[q]);
         if (d.update_out) {
             Vals4 ov;
 #pragma unroll
@@ -352,27 +388,36 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
     }
 }
 
-template <bool NS_F32>
+template <bool NS_F32, int TH, int TW>
+__device__ __forceinline__ void apply_dispatch(const MatDesc& d, int lt, int parity, float decay,
+                                               float step, float qk_tau, float* tileT) {
+    const bool pbf = d.param_dtype == MUON_BF16;
+    if (d.vec4) {
+        if (pbf) apply_tile<true, NS_F32, TH, TW, true>(d, lt, parity, decay, step, qk_tau, tileT);
+        else apply_tile<true, NS_F32, TH, TW, false>(d, lt, parity, decay, step, qk_tau, tileT);
+    } else {
+        if (pbf) apply_tile<false, NS_F32, TH, TW, true>(d, lt, parity, decay, step, qk_tau, tileT);
+        else apply_tile<false, NS_F32, TH, TW, false>(d, lt, parity, decay, step, qk_tau, tileT);
+    }
+}
+
+template <bool NS_F32, bool LDS>
 __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ descs, int n,
                                                     const int32_t* __restrict__ prefix,
                                                     int parity, float decay, float step,
                                                     float qk_tau) {
-    __shared__ float tileT[NS_F32 ? 1 : kEwTile][kEwTile + 1];
+    // the fp32 iteration keeps X^T: no transposing through LDS
+    __shared__ float tileT[NS_F32 ? 1 : ew_lds_floats<false, LDS>()];
     const int tile = blockIdx.x;
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     const int lt = tile - prefix[mi];
-    if (d.ew_th == 16) {
-        if (d.vec4)
-            apply_tile<true, NS_F32, 16>(d, lt, parity, decay, step, qk_tau, tileT);
-        else
-            apply_tile<false, NS_F32, 16>(d, lt, parity, decay, step, qk_tau, tileT);
-    } else {
-        if (d.vec4)
-            apply_tile<true, NS_F32, kEwTile>(d, lt, parity, decay, step, qk_tau, tileT);
-        else
-            apply_tile<false, NS_F32, kEwTile>(d, lt, parity, decay, step, qk_tau, tileT);
-    }
+    if (NS_F32)
+        apply_dispatch<true, kEwTile, kEwTile>(d, lt, parity, decay, step, qk_tau, tileT);
+    else if (!LDS)
+        apply_dispatch<false, 16, 256>(d, lt, parity, decay, step, qk_tau, tileT);
+    else
+        apply_dispatch<false, kTrTH, kTrTW>(d, lt, parity, decay, step, qk_tau, tileT);
 }
 
 // ------------------------------------------------------ table upload ----
@@ -561,12 +606,16 @@ hipError_t launch_clip_finalize(const float* partials, int nblocks, float max_no
     return hipGetLastError();
 }
 
-hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
-                           int nesterov, int ns_f32, hipStream_t st) {
-    if (ns_f32)
-        momentum_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, mu, nesterov);
-    else
-        momentum_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, mu, nesterov);
+hipError_t launch_momentum(const MatDesc* d, int n, const EwGroups& g, float mu, int nesterov,
+                           int ns_f32, hipStream_t st) {
+    if (g.tiles[0] > 0)  // streaming tiles occur only with the bf16 iteration
+        momentum_kernel<false, false><<<g.tiles[0], 256, 0, st>>>(d, n, g.prefix[0], mu, nesterov);
+    if (g.tiles[1] > 0) {
+        if (ns_f32)
+            momentum_kernel<true, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], mu, nesterov);
+        else
+            momentum_kernel<false, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], mu, nesterov);
+    }
     return hipGetLastError();
 }
 
@@ -575,13 +624,20 @@ hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t 
     return hipGetLastError();
 }
 
-hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
-                        float lr, float wd, float qk_tau, int ns_f32, hipStream_t st) {
+hipError_t launch_apply(const MatDesc* d, int n, const EwGroups& g, int final_parity, float lr,
+                        float wd, float qk_tau, int ns_f32, hipStream_t st) {
     const float decay = 1.f - lr * wd;
-    if (ns_f32)
-        apply_kernel<true><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr, qk_tau);
-    else
-        apply_kernel<false><<<total_tiles, 256, 0, st>>>(d, n, p.ew, final_parity, decay, lr, qk_tau);
+    if (g.tiles[0] > 0)
+        apply_kernel<false, false><<<g.tiles[0], 256, 0, st>>>(d, n, g.prefix[0], final_parity,
+                                                              decay, lr, qk_tau);
+    if (g.tiles[1] > 0) {
+        if (ns_f32)
+            apply_kernel<true, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], final_parity,
+                                                                decay, lr, qk_tau);
+        else
+            apply_kernel<false, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], final_parity,
+                                                                 decay, lr, qk_tau);
+    }
     return hipGetLastError();
 }
 

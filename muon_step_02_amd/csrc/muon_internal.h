@@ -44,9 +44,13 @@ __device__ __forceinline__ void gst(T* p, const T& v) {
 constexpr int kPadBf16 = 256;
 constexpr int kSmallBf16 = 128;
 constexpr int kPadF32 = 64;
-// Elementwise kernels (momentum, apply) work on tiles of 4096 elements of the
-// weight: 64 x 64 where Y is needed transposed, else 16 x 256.
+// Elementwise kernels (momentum, apply) work on tiles of the weight:
+// 16 x 256 where the bf16 iteration reads Y as it is; kTrTH x kTrTW, through
+// LDS, where it reads Y^T (or the padded width is not a multiple of 256);
+// kEwTile x kEwTile for the fp32 iteration.  Padded dimensions are multiples
+// of every tile edge used on them.
 constexpr int kEwTile = 64;
+constexpr int kTrTH = 64, kTrTW = 128;
 
 // One matrix as the kernels see it.  Built on the host, copied into the
 // workspace once per call.
@@ -65,9 +69,9 @@ struct MatDesc {
     int32_t transposed;  // rows > cols: the iteration runs on W^T
     int32_t mp, np;      // padded canonical dims: m' = min, n' = max
     int32_t rows_pad, cols_pad;
-    int32_t ew_th;       // elementwise tile height: kEwTile (square) or 16 (16 x 256)
-    int32_t ew_tiles_c;  // elementwise tiles along cols_pad
-    int32_t ew_tiles;    // elementwise tiles of this matrix
+    int32_t ew_th, ew_tw;  // elementwise tile: 16 x 256, kTrTH x kTrTW or kEwTile x kEwTile
+    int32_t ew_tiles_c;    // elementwise tiles along cols_pad
+    int32_t ew_tiles;      // elementwise tiles of this matrix (one norm partial each)
     int32_t vec4;        // 1: every row start of param/grad/mom is 16B aligned and cols % 4 == 0
     float scale;         // shape multiplier * extra_scale
     // workspace buffers (bf16 or f32 elements by ns dtype)
@@ -82,9 +86,18 @@ struct MatDesc {
 // Grouped launches: workgroup -> (matrix, local tile) through prefix sums of
 // tiles per matrix (int32 entries, n+1 of them).
 struct Prefix {
-    const int32_t* ew;
     const int32_t* gram;  // triangle tiles (Gram and polynomial)
     const int32_t* upd;   // full tiles of the update
+};
+
+// Elementwise tiles by kind: 0 streaming (16 x 256), 1 through LDS (the
+// transposing and the fp32 shapes).  Each kind is its own launch, so the
+// streaming kernel keeps the occupancy of its small register and LDS
+// footprint; its prefix runs over all matrices, those of the other kind
+// having no tiles in it.
+struct EwGroups {
+    const int32_t* prefix[2];
+    int tiles[2];
 };
 
 __device__ __forceinline__ int find_matrix(const int32_t* prefix, int n, int32_t tile) {
@@ -121,11 +134,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // kernel arguments, kTableChunkWords words per launch.
 constexpr int kTableChunkWords = 512;
 hipError_t launch_table_upload(const void* host, size_t bytes, void* dst, hipStream_t st);
-hipError_t launch_momentum(const MatDesc* d, int n, Prefix p, int total_tiles, float mu,
-                           int nesterov, int ns_f32, hipStream_t st);
+hipError_t launch_momentum(const MatDesc* d, int n, const EwGroups& g, float mu, int nesterov,
+                           int ns_f32, hipStream_t st);
 hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t st);
-hipError_t launch_apply(const MatDesc* d, int n, Prefix p, int total_tiles, int final_parity,
-                        float lr, float wd, float qk_tau, int ns_f32, hipStream_t st);
+hipError_t launch_apply(const MatDesc* d, int n, const EwGroups& g, int final_parity, float lr,
+                        float wd, float qk_tau, int ns_f32, hipStream_t st);
 
 // bf16 Newton-Schulz phases over all matrices.  `it` is the iteration index
 // (0-based): it selects the ping-pong buffers and, for it == 0, folds the
