@@ -23,9 +23,9 @@
 // está cambiando" (gustavoai.dev), sections "Adam: las dos ideas juntas" and
 // "La W: un error de regularización que duró tres años".
 //
-// Each workgroup of the Muon kernels owns one 64 x 64 tile of one weight;
-// 256 threads, each thread four rows of four consecutive columns, so a wave
-// reads four 256-byte row segments per instruction (fp32).
+// Each workgroup of the Muon kernels owns one tile of one weight (see
+// EwTile for the shapes); the AdamW kernels take chunks of kAdamwChunk
+// elements of one tensor.
 #include <string.h>
 
 #include "muon_internal.h"
@@ -178,8 +178,6 @@ struct EwTile {
 // LDS tile for the transposing shapes: TW rows of TH + 1 floats (the +1 keeps
 // both the column writes and the row reads on distinct banks).
 constexpr int lds_tile(int th, int tw) { return tw * (th + 1); }
-constexpr int kLdsT = lds_tile(kTrTH, kTrTW) > lds_tile(kEwTile, kEwTile)
-                          ? lds_tile(kTrTH, kTrTW) : lds_tile(kEwTile, kEwTile);
 
 template <bool VEC, bool NS_F32, int TH, int TW, bool GBF>
 __device__ __forceinline__ void momentum_tile(const MatDesc& d, int lt, float mu, int nesterov,
