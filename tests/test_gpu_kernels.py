@@ -111,8 +111,12 @@ def _rand_matrix_inputs(rows, cols, seed, pdt=torch.float32, gdt=torch.float32, 
     return W, G, M
 
 
+# (64, 300): short side <= 128 with a padded width of 384, not a multiple of 256,
+# so its elementwise tiles go through LDS without a transpose; (1030, 513): a
+# tall matrix whose rows are not 16-byte aligned (scalar path of the
+# transposing tiles).
 MIXED = [(256, 256), (300, 500), (500, 300), (1, 1), (1, 37), (37, 1), (7, 13), (1024, 256),
-         (256, 1024), (513, 1030), (64, 64)]
+         (256, 1024), (513, 1030), (64, 64), (64, 300), (300, 64), (1030, 513)]
 
 BASE_HP = dict(lr=2e-4, mu=0.95, weight_decay=0.1, nesterov=True, eps=1e-7, steps=5,
                scale_mode="moonlight", extra_scale=1.0, ns_dtype="bf16")
