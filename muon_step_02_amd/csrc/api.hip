@@ -3,9 +3,9 @@
 //
 // One call of muon_step_batched enqueues, on the caller's stream:
 //   the descriptor-table upload (kernel arguments -> workspace, 2 KB a launch),
-//   momentum (all matrices), norm finalize (all matrices),
-//   ns_steps x {gram, poly, update} (each one grouped launch over all matrices),
-//   apply (all matrices).
+//   momentum (one launch per elementwise tile kind in use), norm finalize,
+//   ns_steps x {gram, poly, update} (one grouped launch per size class in use),
+//   apply (one launch per elementwise tile kind in use).
 // The launch count does not depend on the number of matrices.  Matrices are
 // ordered by descending Newton-Schulz work in the table so the biggest tiles
 // are dispatched first.
@@ -141,8 +141,9 @@ bool aligned_rows(const void* p, int64_t ld, size_t es) {
 // their own GEMM tile size: "large" (256-wide tiles and padding) and, for
 // bf16 Newton-Schulz, "small" (short side <= 128: 128-wide tiles and
 // padding).  The descriptor table holds the large class first; each class has
-// its own prefix arrays of Gram/polynomial and update tiles, while the
-// elementwise kernels run over all matrices at once.
+// its own prefix arrays of Gram/polynomial and update tiles.  The elementwise
+// kernels run over all matrices, one launch per tile kind (streaming, or
+// through LDS), each with a prefix array of its own.
 struct ClassPlan {
     int first = 0, count = 0;           // descriptor range
     std::vector<int32_t> pgram, pupd;   // count + 1 entries each
