@@ -183,8 +183,8 @@ muon_status muon_workspace_size(muon_handle h, const muon_matrix* mats, int n,
  * no reference to host memory, so it may be captured in a graph (a replay
  * runs the captured shapes and pointers on the buffers' contents at replay
  * time).  Rejects:
- * n < 1, rows or cols < 1, ld < cols, a null param/grad/momentum, an unknown
- * dtype or mode, ns_steps < 1, lr/momentum non-finite, overlapping
+ * n < 1, rows or cols < 1 or > 2^20, ld < cols, a null param/grad/momentum, an
+ * unknown dtype or mode, ns_steps < 1 or > 1000, lr/momentum non-finite, overlapping
  * param/grad/momentum ranges within a matrix, a small or null workspace,
  * qk_block_rows outside [1, rows] when qk_smax is set, qk_tau < 0. */
 muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,

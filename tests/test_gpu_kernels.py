@@ -265,6 +265,17 @@ def _status(fn):
     return 0
 
 
+def test_largest_dimension():
+    # the longest side the ABI accepts (2^20), as a row and as a column: one
+    # 128-wide Gram tile with K = 2^20, and 8192 update tiles
+    _run_and_compare([(1, 1 << 20), (1 << 20, 1)], BASE_HP, TOL_O_BF16, seed=9)
+    h = Handle.get()
+    W, G, M = (torch.zeros(1, (1 << 20) + 1, device=DEV) for _ in range(3))
+    with pytest.raises(mu.MuonError) as e:
+        mu.muon_workspace_size(h, [mu.muon_matrix(W, G, M)], hp_from(BASE_HP))
+    assert e.value.status == 1
+
+
 def test_abi_validation_rejects_and_enqueues_nothing():
     h = Handle.get()
     W, G, M = _rand_matrix_inputs(256, 256, 1)
