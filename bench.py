@@ -102,8 +102,8 @@ def cpu_baseline(wl, budget_s=20.0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the Muon step shards by whole matrices across GPUs, see the design notes)"
+        print("bench.py: measures one GPU only; --gpus %d is not supported (across GPUs the "
+              "Muon step shards by whole matrices, each GPU running the library on its share)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
