@@ -339,8 +339,10 @@ hipEvent_t take_event(muon_context* h) {
         h->event_pool.pop_back();
         return e;
     }
+    // timing only: no system-scope fence (its cache writeback would slow the
+    // launches being timed); the host reads nothing but the timestamps
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
