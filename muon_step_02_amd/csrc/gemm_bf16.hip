@@ -392,8 +392,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                         read_frags<C, QKN>(st, (u + 1) % C::NS, 0, wm, wn, frow, khalf, lane, f[0]);
                     }
                     mfma_frags<C>(acc, f[kk & 1]);
-                    // the k-major reads are twice as many: front-load them
-                    interleave_reads_mfma<C::FM + (QKN ? 2 : 1) * C::FN, C::FM * C::FN, QKN ? 2 : 1>();
+                    // two reads with each of the first MFMAs: the reads go out early
+                    // (k-major fragments are two reads each)
+                    interleave_reads_mfma<C::FM + (QKN ? 2 : 1) * C::FN, C::FM * C::FN, 2>();
                 }
             }
         }
