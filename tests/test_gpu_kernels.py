@@ -12,7 +12,7 @@ import torch
 import oracle
 import muon_step_02_amd as mu
 from harness import (TOL_O_BF16, TOL_O_F32, TOL_STATE, Handle, compare_matrix, f64, hp_from,
-                     relF, run_muon_step)
+                     oracle_kwargs, recipe_floor_output, relF, run_muon_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,7 +123,8 @@ BASE_HP = dict(lr=2e-4, mu=0.95, weight_decay=0.1, nesterov=True, eps=1e-7, step
 
 
 def _run_and_compare(shapes, hpd, tol_o, pdt=torch.float32, gdt=torch.float32, seed=0,
-                     lowrank=True):
+                     lowrank=True, tol_for=None):
+    # tol_for(k, W0, G0, M0), if given, sets matrix k's output tolerance
     ins, mats, outs = [], [], []
     for k, (r, c) in enumerate(shapes):
         W, G, M = _rand_matrix_inputs(r, c, seed * 1000 + k, pdt, gdt, lowrank)
@@ -144,7 +145,8 @@ def _run_and_compare(shapes, hpd, tol_o, pdt=torch.float32, gdt=torch.float32, s
             assert relF(f64(M), Mr) <= TOL_STATE
             assert relF(f64(W), Wr) <= 2 ** -8
         else:
-            compare_matrix(W0, G0, M0, f64(W), f64(M), f64(O), hpd, tol_o, report, str(shapes[k]))
+            tol_k = tol_o if tol_for is None else tol_for(k, W0, G0, M0)
+            compare_matrix(W0, G0, M0, f64(W), f64(M), f64(O), hpd, tol_k, report, str(shapes[k]))
         Mr = oracle.momentum_update(M0, G0, hpd["mu"])
         Yr = oracle.nesterov_blend(G0, Mr, hpd["mu"], hpd["nesterov"])
         assert abs(float(nrm.item()) - np.linalg.norm(Yr)) <= 1e-5 * np.linalg.norm(Yr) + 1e-30
@@ -172,6 +174,49 @@ def test_step_mixed_batch_bf16():
 
 def test_step_mixed_batch_f32():
     _run_and_compare(MIXED, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=12)
+
+
+@pytest.mark.parametrize("ns_dtype,count", [("bf16", 2500), ("fp32", 600)])
+def test_step_thousands_of_tiny_matrices_in_one_call(ns_dtype, count):
+    # Ragged matrices of at most 48 x 48 beside two large ones: the descriptor
+    # table goes up in hundreds of chunks, the tile prefix search runs over
+    # thousands of entries, and almost every matrix is one tile.
+    #
+    # bf16 iteration: a matrix of a few dozen elements has a bf16 floor near
+    # the 3e-2 bar itself (the recipe run in bf16 on such inputs misses 3e-2
+    # in 30-80% of cases; on the workloads' matrices it stays near 1.8e-2).
+    # A tiny matrix is held to 3e-2 or to 1.5x the error of that recipe on
+    # its own input, whichever is larger: the kernels round at other points
+    # (fp32 accumulation and epilogues), so on one input either may come out
+    # ahead.  The two large matrices keep the plain 3e-2, and over all tiny
+    # matrices the kernels must beat the recipe clearly (median ratio < 0.75).
+    rng = np.random.default_rng(2024)
+    shapes = [tuple(int(v) for v in rng.integers(1, 49, size=2)) for _ in range(count)]
+    shapes[count // 2:count // 2] = [(300, 500)]
+    shapes.append((1030, 513))
+    hpd = dict(BASE_HP, ns_dtype=ns_dtype)
+    if ns_dtype == "fp32":
+        _run_and_compare(shapes, hpd, TOL_O_F32, seed=13)
+        return
+    kw = oracle_kwargs(hpd)
+    ratios = []
+
+    def tol_for(k, W0, G0, M0):
+        if max(shapes[k]) > 48:
+            return TOL_O_BF16
+        Mr = oracle.momentum_update(M0, G0, kw["mu"])
+        Y = oracle.nesterov_blend(G0, Mr, kw["mu"], kw["nesterov"])
+        Oref = oracle.newton_schulz(Y, steps=kw["steps"], eps=kw["eps"])
+        floor = relF(recipe_floor_output(Y, steps=kw["steps"], eps=kw["eps"]), Oref)
+        ratios.append((k, floor))
+        return max(TOL_O_BF16, 1.5 * floor)
+
+    report = _run_and_compare(shapes, hpd, TOL_O_BF16, seed=13, tol_for=tol_for)
+    floors = dict(ratios)
+    r = np.array([e / floors[k] for k, (_, _, e, _, _, _) in enumerate(report) if k in floors])
+    print("tiny bf16 matrices: kernel/recipe error ratio median %.2f, p90 %.2f, max %.2f"
+          % (np.median(r), np.quantile(r, 0.9), r.max()))
+    assert np.median(r) < 0.75
 
 
 @pytest.mark.parametrize("mode", ["moonlight", "jordan", "bernstein", "none"])
