@@ -176,6 +176,15 @@ def test_step_mixed_batch_f32():
     _run_and_compare(MIXED, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=12)
 
 
+@pytest.mark.parametrize("ns_dtype,steps", [("bf16", 2), ("bf16", 4), ("fp32", 6)])
+def test_even_iteration_counts(ns_dtype, steps):
+    # after an even number of iterations the result sits in the other
+    # ping-pong buffer than after an odd one; apply must read that one
+    shapes = [(300, 500), (500, 300), (64, 300), (300, 64), (1030, 513)]
+    tol = TOL_O_BF16 if ns_dtype == "bf16" else TOL_O_F32
+    _run_and_compare(shapes, dict(BASE_HP, ns_dtype=ns_dtype, steps=steps), tol, seed=21 + steps)
+
+
 @pytest.mark.parametrize("ns_dtype,count", [("bf16", 2500), ("fp32", 600)])
 def test_step_thousands_of_tiny_matrices_in_one_call(ns_dtype, count):
     # Ragged matrices of at most 48 x 48 beside two large ones: the descriptor
