@@ -291,6 +291,47 @@ def test_repeatable_bitwise():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("ns_dtype", ["bf16", "fp32"])
+def test_workspace_garbage_and_reuse_across_batches(ns_dtype):
+    # The workspace starts as all-ones bytes (NaN in every float view) and
+    # serves two differently shaped batches in a row.  The second batch must
+    # match, bit for bit, the same batch run on a fresh zeroed workspace: no
+    # kernel may read workspace memory that this call did not write first
+    # (padding, partial sums, tables).
+    h = Handle.get()
+    hp = hp_from(dict(BASE_HP, ns_dtype=ns_dtype))
+    shapes_a = [(300, 500), (64, 300), (1030, 513)]
+    shapes_b = [(500, 300), (37, 1), (256, 1024), (300, 64)]
+
+    def batch(shapes, seed):
+        ts = [_rand_matrix_inputs(r, c, seed + k) for k, (r, c) in enumerate(shapes)]
+        outs = [torch.empty_like(W) for W, _, _ in ts]
+        mats = [mu.muon_matrix(W, G, M, update_out=O) for (W, G, M), O in zip(ts, outs)]
+        return ts, outs, mats
+
+    ta, oa, ma = batch(shapes_a, 500)
+    tb, ob, mb = batch(shapes_b, 600)
+    tb0 = [tuple(t.clone() for t in x) for x in tb]
+    need = max(mu.muon_workspace_size(h, ma, hp), mu.muon_workspace_size(h, mb, hp))
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=DEV)
+    run_muon_step(ma, hp, ws=ws)
+    run_muon_step(mb, hp, ws=ws)
+    torch.cuda.synchronize()
+
+    tc = [tuple(t.clone() for t in x) for x in tb0]
+    oc = [torch.empty_like(W) for W, _, _ in tc]
+    mc = [mu.muon_matrix(W, G, M, update_out=O) for (W, G, M), O in zip(tc, oc)]
+    run_muon_step(mc, hp, ws=torch.zeros(need, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    tol = TOL_O_BF16 if ns_dtype == "bf16" else TOL_O_F32
+    for k in range(len(shapes_b)):
+        assert torch.equal(ob[k], oc[k]) and torch.equal(tb[k][0], tc[k][0])
+        assert torch.equal(tb[k][2], tc[k][2])
+        W0, G0, M0 = (f64(t) for t in tb0[k])
+        compare_matrix(W0, G0, M0, f64(tb[k][0]), f64(tb[k][2]), f64(ob[k]),
+                       dict(BASE_HP, ns_dtype=ns_dtype), tol)
+
+
 def test_consecutive_steps_carry_momentum():
     W, _, M = _rand_matrix_inputs(512, 256, 41)
     M.zero_()
