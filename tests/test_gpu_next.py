@@ -152,7 +152,8 @@ def test_adamw_global_norm_clipping(scale, gdt):
         grads = [(torch.randn(n, generator=g, device=DEV) * scale).to(gdt) for n in sizes]
         ts = [mu.adamw_tensor(p, gr, m, v) for p, gr, m, v in zip(P, grads, Ms, Vs)]
         if ws is None:
-            ws = torch.empty(mu.adamw_workspace_size(h, ts), dtype=torch.uint8, device=DEV)
+            # all-ones bytes: every partial sum must be written before it is read
+            ws = torch.full((mu.adamw_workspace_size(h, ts),), 255, dtype=torch.uint8, device=DEV)
         mu.adamw_step_clipped(h, ts, mu.adamw_hparams(step=t, **ADAMW_HP), 1.0, ws, norm_out)
         torch.cuda.synchronize()
         G64 = [f64(gr) for gr in grads]
