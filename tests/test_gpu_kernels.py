@@ -176,6 +176,15 @@ def test_step_mixed_batch_f32():
     _run_and_compare(MIXED, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=12)
 
 
+@pytest.mark.parametrize("ns_dtype", ["bf16", "fp32"])
+def test_small_and_large_class_boundary(ns_dtype):
+    # short side 128 is the last of the 128-tile class, 129 the first of the
+    # 256-tile class; both orientations, one call
+    shapes = [(128, 700), (129, 700), (700, 128), (700, 129), (128, 128), (129, 129), (256, 129)]
+    tol = TOL_O_BF16 if ns_dtype == "bf16" else TOL_O_F32
+    _run_and_compare(shapes, dict(BASE_HP, ns_dtype=ns_dtype), tol, seed=31)
+
+
 @pytest.mark.parametrize("ns_dtype,steps", [("bf16", 2), ("bf16", 4), ("fp32", 6)])
 def test_even_iteration_counts(ns_dtype, steps):
     # after an even number of iterations the result sits in the other
