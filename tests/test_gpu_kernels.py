@@ -254,6 +254,11 @@ def test_bf16_grad_and_bf16_param():
     _run_and_compare([(256, 384), (384, 256)], BASE_HP, TOL_O_BF16, gdt=torch.bfloat16, seed=6)
     _run_and_compare([(256, 384), (384, 256)], BASE_HP, TOL_O_BF16, pdt=torch.bfloat16,
                      gdt=torch.bfloat16, seed=8)
+    # rows not 16-byte aligned (scalar paths), the small class, both orientations
+    ragged = [(37, 1), (7, 13), (1030, 513), (513, 1030), (64, 300), (300, 64)]
+    _run_and_compare(ragged, BASE_HP, TOL_O_BF16, pdt=torch.bfloat16, gdt=torch.bfloat16, seed=9)
+    _run_and_compare(ragged, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, gdt=torch.bfloat16,
+                     seed=10)
 
 
 def test_row_blocks_of_fused_tensor():
