@@ -177,6 +177,38 @@ def test_step_mixed_batch_f32():
 
 
 @pytest.mark.parametrize("ns_dtype", ["bf16", "fp32"])
+def test_strided_views_leave_the_rest_untouched(ns_dtype):
+    # Column slices of wider buffers: param, grad and momentum each with its
+    # own leading dimension, some of them odd (rows not 16-byte aligned), one
+    # gradient in bf16.  Columns beyond the view hold a sentinel that must
+    # survive the step.
+    cases = [((300, 500), (512, 700, 600), torch.float32),
+             ((500, 300), (301, 333, 450), torch.float32),
+             ((64, 300), (303, 300, 320), torch.bfloat16),
+             ((1030, 513), (600, 515, 513), torch.float32)]
+    hpd = dict(BASE_HP, ns_dtype=ns_dtype)
+    mats, keep = [], []
+    for k, ((r, c), (lw, lg, lm), gdt) in enumerate(cases):
+        W, G, M = _rand_matrix_inputs(r, c, 700 + k, gdt=gdt)
+        bufs = [torch.full((r, ld), 7.0, dtype=t.dtype, device=DEV) for t, ld in
+                ((W, lw), (G, lg), (M, lm))]
+        views = [b[:, :c] for b in bufs]
+        for v, t in zip(views, (W, G, M)):
+            v.copy_(t)
+        O = torch.empty(r, c, device=DEV)
+        mats.append(mu.muon_matrix(*views, update_out=O))
+        keep.append((tuple(f64(t) for t in (W, G, M)), bufs, views, O))
+    run_muon_step(mats, hp_from(hpd))
+    torch.cuda.synchronize()
+    tol = TOL_O_BF16 if ns_dtype == "bf16" else TOL_O_F32
+    for ((W0, G0, M0), bufs, (W, G, M), O), ((r, c), _, _) in zip(keep, cases):
+        compare_matrix(W0, G0, M0, f64(W), f64(M), f64(O), hpd, tol)
+        assert np.array_equal(f64(G), G0)
+        for b in bufs:
+            assert bool((b[:, c:] == 7.0).all())
+
+
+@pytest.mark.parametrize("ns_dtype", ["bf16", "fp32"])
 def test_small_and_large_class_boundary(ns_dtype):
     # short side 128 is the last of the 128-tile class, 129 the first of the
     # 256-tile class; both orientations, one call
