@@ -28,6 +28,9 @@ web page and the section on it:
 * "Why Muon Works" (r00kie-liu.github.io) -- section 7.1 (parameter routing),
   7.3 (QKV split) and 7.6 (starter configuration).
 
+``storage.round_to_bf16`` rounds a result to bfloat16 for parameters kept in
+that format (round to nearest, ties to even), from the format's definition.
+
 Pins: every function here is checked by ``tests/test_oracle_pins.py``
 against closed forms (the SVD form of the odd polynomial, momentum and Adam
 recurrences), numbers the pages print (tests/golden/) and invariants
@@ -46,6 +49,7 @@ from .muon import (
     qk_clip,
 )
 from .adamw import adamw_tensor_step, adamw_step, clip_by_global_norm
+from .storage import round_to_bf16, store
 
 __all__ = [
     "MUON_COEFFS",
@@ -59,4 +63,6 @@ __all__ = [
     "adamw_tensor_step",
     "adamw_step",
     "clip_by_global_norm",
+    "round_to_bf16",
+    "store",
 ]

@@ -21,16 +21,20 @@ this follows its prose:
 
 import numpy as np
 
+from .storage import store
+
 
 def adamw_tensor_step(theta, g, m, v, *, step, lr, beta1=0.9, beta2=0.95,
-                      eps=1e-8, weight_decay=0.1):
+                      eps=1e-8, weight_decay=0.1, param_dtype="fp32"):
     """One AdamW update of one tensor.  ``step`` is t >= 1 (already counted).
 
     Returns ``(theta_new, m_new, v_new)``; every operation is elementwise:
 
     ``m = b1 m + (1-b1) g``; ``v = b2 v + (1-b2) g^2``;
     ``m_hat = m / (1-b1^t)``; ``v_hat = v / (1-b2^t)``;
-    ``theta = theta - lr * (m_hat / (sqrt(v_hat) + eps) + wd * theta_old)``.
+    ``theta = theta - lr * (m_hat / (sqrt(v_hat) + eps) + wd * theta_old)``;
+    a ``param_dtype="bf16"`` parameter stores theta rounded once to bfloat16
+    (:func:`oracle.storage.store`); the moments are fp32 state.
     """
     if step < 1:
         raise ValueError("AdamW step count starts at 1")
@@ -44,7 +48,7 @@ def adamw_tensor_step(theta, g, m, v, *, step, lr, beta1=0.9, beta2=0.95,
     v_hat = v_new / (1.0 - beta2 ** step)
     direction = m_hat / (np.sqrt(v_hat) + eps)
     theta_new = theta - lr * (direction + weight_decay * theta)
-    return theta_new, m_new, v_new
+    return store(theta_new, param_dtype), m_new, v_new
 
 
 def clip_by_global_norm(grads, max_norm):

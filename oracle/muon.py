@@ -12,6 +12,8 @@ upcast exactly.
 
 import numpy as np
 
+from .storage import store
+
 # Quintic coefficients (a, b, c) of p(s) = a s + b s^3 + c s^5, used for every
 # iteration.  "The Optimizer Wars ...", section "What is Muon? Momentum
 # orthogonalized by Newton-Schulz"; "About Muon: Why Not Adam", section
@@ -51,20 +53,26 @@ def nesterov_blend(G, M_new, mu, nesterov=True):
     return (1.0 - mu) * _f64(G) + mu * M_new
 
 
+def _gram_polynomial(S, a, b, c):
+    """``a I + b S + c S^2`` for a symmetric Gram matrix ``S``, in Horner form
+    ``a I + S (b I + c S)``."""
+    eye = np.eye(S.shape[0])
+    return a * eye + S @ (b * eye + c * S)
+
+
 def newton_schulz(G, steps=5, eps=1e-7, coeffs=None):
     """Approximate polar factor of ``G`` by iterated odd quintic polynomials.
 
-    Steps, in the order "About Muon: Why Not Adam" gives them (sections
-    "Making It Actually Run" and "The whole thing, in about forty lines"):
-
-    1. divide by the Frobenius norm plus ``eps`` so that every singular value
-       lies in (0, 1] (the norm bounds the largest singular value);
-    2. if the matrix has more rows than columns, work on its transpose so that
-       the Gram matrix is the small one (the short-side transpose);
-    3. ``steps`` times: ``A = X X^T``, ``B = b A + c A A``, ``X = a X + B X``,
-       which is ``X <- a X + b (X X^T) X + c (X X^T)^2 X``, the odd
-       polynomial of the lemma written on the small Gram;
-    4. transpose back if step 2 transposed.
+    "About Muon: Why Not Adam", section "Making It Actually Run": after
+    scaling by the Frobenius norm plus ``eps`` (the norm bounds the largest
+    singular value, so every singular value lands in (0, 1]), each iteration
+    replaces ``X`` by the odd matrix polynomial ``p(X) = a X + b X X^T X +
+    c (X X^T)^2 X``, which maps each singular value ``s`` to ``a s + b s^3 +
+    c s^5`` and leaves the singular vectors alone.  The polynomial only needs
+    a Gram matrix, and the section takes it on the short side: for a wide
+    ``X`` (rows <= cols), ``p(X) = q(X X^T) X``; for a tall one, ``p(X) =
+    X q(X^T X)``, with ``q(S) = a I + b S + c S^2``.  Both are the same
+    matrix; the short side only makes ``S`` small.
 
     ``coeffs`` is either one triple used for every iteration (default: the
     Muon triple) or a sequence of ``steps`` triples, one per iteration.
@@ -82,20 +90,13 @@ def newton_schulz(G, steps=5, eps=1e-7, coeffs=None):
             raise ValueError("per-iteration coefficients must have shape (steps, 3)")
         schedule = [tuple(row) for row in coeffs]
 
-    frob = np.sqrt(np.sum(X * X))
-    X = X / (frob + eps)
-
-    transposed = X.shape[0] > X.shape[1]
-    if transposed:
-        X = X.T
-
+    X = X / (np.sqrt(np.sum(X * X)) + eps)
+    wide = X.shape[0] <= X.shape[1]
     for a, b, c in schedule:
-        A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
-
-    if transposed:
-        X = X.T
+        if wide:
+            X = _gram_polynomial(X @ X.T, a, b, c) @ X
+        else:
+            X = X @ _gram_polynomial(X.T @ X, a, b, c)
     return np.ascontiguousarray(X)
 
 
@@ -148,7 +149,8 @@ def qk_clip(W, s_max, tau, block_rows):
 
 def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
                      eps=1e-7, steps=5, coeffs=None, scale_mode="moonlight",
-                     extra_scale=1.0, qk_smax=None, qk_block_rows=0, qk_tau=100.0):
+                     extra_scale=1.0, qk_smax=None, qk_block_rows=0, qk_tau=100.0,
+                     param_dtype="fp32"):
     """One Muon step for one weight matrix; returns ``(W_new, M_new, O)``.
 
     Order of operations ("About Muon: Why Not Adam", section "The whole thing,
@@ -163,7 +165,9 @@ def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
     5. ``W <- (1 - lr*wd) W`` (decay uses the weight before the update), then
        ``W <- W - lr * s * O``;
     6. with ``qk_smax`` given, :func:`qk_clip` on the updated weight
-       (MuonClip: the clip follows the ordinary Muon update).
+       (MuonClip: the clip follows the ordinary Muon update);
+    7. a ``param_dtype="bf16"`` weight stores the result of 5-6 rounded
+       once to bfloat16 (:func:`oracle.storage.store`).
 
     ``O`` is the orthogonalised update before the multiplier, returned so
     tests can compare it directly.
@@ -178,7 +182,7 @@ def muon_matrix_step(W, G, M, *, lr, mu=0.95, weight_decay=0.0, nesterov=True,
     W_new = W_new - (lr * s) * O
     if qk_smax is not None:
         W_new = qk_clip(W_new, qk_smax, qk_tau, qk_block_rows)
-    return W_new, M_new, O
+    return store(W_new, param_dtype), M_new, O
 
 
 def muon_step(weights, grads, moms, **hparams):

@@ -67,29 +67,27 @@ def hp_from(muon_hp, **over):
 
 
 def recipe_floor_output(Y, steps=5, eps=1e-7, coeffs=None):
-    """The Newton-Schulz recipe run the way a plain bf16 implementation runs
-    it: every tensor held in bf16, products accumulated in fp32 and rounded,
+    """The Newton-Schulz method as a plain bf16 implementation computes it:
+    every tensor held in bf16, each product accumulated in fp32 and rounded,
     every elementwise result rounded ("About Muon: Why Not Adam", section
-    "Making It Actually Run", iterated in bf16 as "The Optimizer Wars ...",
-    section "What is Muon?" describes).  On the CPU, on the NS input Y.  Its
-    distance to the oracle is the error floor such an implementation has on
-    this input; reported beside the kernels' error, never used as a
-    reference."""
+    "Making It Actually Run", in the bf16 that "The Optimizer Wars ...",
+    section "What is Muon?" names).  The odd polynomial goes through the
+    short-side Gram, q(X X^T) X for a wide X or X q(X^T X) for a tall one.
+    On the CPU, on the NS input Y.  Its distance to the oracle is the error
+    floor such an implementation has on this input; reported beside the
+    kernels' error, never used as a reference."""
     def r(t):
         return t.to(torch.bfloat16).to(torch.float32)
     X = r(torch.from_numpy(np.ascontiguousarray(Y, dtype=np.float32)))
-    tr = X.shape[0] > X.shape[1]
-    if tr:
-        X = X.T.contiguous()
     X = r(X / (r(torch.linalg.norm(X)) + eps))
+    wide = X.shape[0] <= X.shape[1]
     sched = ([tuple(c) for c in np.asarray(coeffs).reshape(-1, 3)] if coeffs is not None
              else [oracle.MUON_COEFFS] * steps)
     for a, b, c in sched:
-        A = r(X @ X.T)
-        B = r(r(b * A) + r(c * r(A @ A)))
-        X = r(r(a * X) + r(B @ X))
-    if tr:
-        X = X.T
+        S = r(X @ X.T) if wide else r(X.T @ X)
+        Q = r(r(b * S) + r(c * r(S @ S)))          # the polynomial's b and c terms
+        QX = r(Q @ X) if wide else r(X @ Q)
+        X = r(r(a * X) + QX)
     return X.double().numpy()
 
 

@@ -167,7 +167,7 @@ def test_rank_one():
 
 
 # --------------------------------------------------------------------------
-# P4, P5: transpose symmetry, the un-transposed (X^T X) form, equivariance
+# P4, P5: transpose symmetry, the long-side Gram form, equivariance
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("shape", [(5, 9), (9, 5), (1, 4), (33, 17)])
@@ -178,15 +178,20 @@ def test_transpose_symmetry(shape):
 
 
 @pytest.mark.parametrize("shape", [(9, 5), (5, 9), (8, 8)])
-def test_lemma_form_without_short_side_transpose(shape):
-    # p(X) = aX + bX(X^T X) + cX(X^T X)^2 -- the lemma's own form, applied to
-    # the normalised matrix as it is, five times.
+def test_lemma_form_on_the_long_side(shape):
+    # p(X) = aX + b X X^T X + c (X X^T)^2 X written through the Gram on the
+    # *long* side (the large one), the route the oracle never takes: X^T X on
+    # the right for a wide or square X, X X^T on the left for a tall one.
     rng = np.random.default_rng(42 + shape[0])
     G = rng.standard_normal(shape)
     X = G / (np.linalg.norm(G, "fro") + 1e-7)
     for _ in range(5):
-        S = X.T @ X
-        X = A_ * X + B_ * (X @ S) + C_ * (X @ S @ S)
+        if shape[0] <= shape[1]:
+            S = X.T @ X
+            X = A_ * X + B_ * (X @ S) + C_ * (X @ S @ S)
+        else:
+            S = X @ X.T
+            X = A_ * X + B_ * (S @ X) + C_ * (S @ S @ X)
     assert np.allclose(oracle.newton_schulz(G), X, atol=1e-13)
 
 
@@ -479,3 +484,47 @@ def test_global_norm_clipping():
     ts, ms, vs = oracle.adamw_step(ts, [g2], ms, vs, max_grad_norm=1.0, step=2, lr=1.0,
                                    weight_decay=0.0)
     assert np.allclose(ms[0], 0.9 * 0.1 * g1 / 50.0 + 0.1 * g2)
+
+
+# --------------------------------------------------------------------------
+# bf16 storage rounding: closed-form ties and torch's conversion
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_closed_forms():
+    # spacing of bf16 in [1, 2) is 2^-7; halfway cases go to the even neighbour
+    h = 2.0 ** -7
+    cases = {1.0: 1.0, 1.0 + h / 2: 1.0, 1.0 + 1.5 * h: 1.0 + 2 * h, 1.0 + 0.49 * h: 1.0,
+             1.0 + 0.51 * h: 1.0 + h, -(1.0 + 1.5 * h): -(1.0 + 2 * h), 0.0: 0.0,
+             2.0 - h / 4: 2.0, 3.0 * 2.0 ** -20: 3.0 * 2.0 ** -20,
+             (1.0 + h / 2) * 2.0 ** 40: 2.0 ** 40}
+    got = oracle.round_to_bf16(np.array(list(cases)))
+    assert np.array_equal(got, np.array(list(cases.values())))
+    assert np.isnan(oracle.round_to_bf16(np.array([np.nan]))[0])
+    assert oracle.round_to_bf16(np.array([-np.inf]))[0] == -np.inf
+
+
+def test_bf16_rounding_matches_torch_conversion():
+    import torch
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal(200000) * 10.0 ** rng.uniform(-30, 30, 200000)).astype(np.float32)
+    # exact ties: float32 values whose low 16 bits are 0x8000
+    bits = rng.integers(0x00800000, 0x7f000000, 20000, dtype=np.uint32)
+    ties = ((bits & 0xffff0000) | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.round_to_bf16(x.astype(np.float64)), want)
+
+
+def test_bf16_parameter_stores_the_rounded_step():
+    rng = np.random.default_rng(18)
+    W = oracle.round_to_bf16(rng.standard_normal((6, 9)) * 0.02)
+    G = rng.standard_normal((6, 9))
+    full, M, O = oracle.muon_matrix_step(W, G, np.zeros_like(W), lr=0.02)
+    low, M2, O2 = oracle.muon_matrix_step(W, G, np.zeros_like(W), lr=0.02, param_dtype="bf16")
+    assert np.array_equal(low, oracle.round_to_bf16(full))
+    assert np.array_equal(M, M2) and np.array_equal(O, O2)
+    th, m, v = oracle.adamw_tensor_step(W, G, np.zeros_like(W), np.zeros_like(W), step=1, lr=1e-3)
+    th2, m2, v2 = oracle.adamw_tensor_step(W, G, np.zeros_like(W), np.zeros_like(W), step=1,
+                                           lr=1e-3, param_dtype="bf16")
+    assert np.array_equal(th2, oracle.round_to_bf16(th))
+    assert np.array_equal(m, m2) and np.array_equal(v, v2)
