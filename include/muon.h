@@ -29,10 +29,11 @@
  * Frontier AI Training", ai.info, section "What is Muon? ...").
  *
  * Threading: a handle may be used by one host thread at a time.  Calls only
- * enqueue work (plus, in muon_step_batched, a small host-to-device copy of
- * the descriptor table from pinned memory the handle owns) and return; they
- * never wait for the device except to recycle one of the handle's pinned
- * descriptor slots (at most 8 calls in flight per handle).
+ * enqueue work and return; they never wait for the device.  muon_step_batched
+ * carries its descriptor table (one 216-byte entry per matrix plus prefix
+ * arrays) into the caller's workspace in the arguments of small upload
+ * kernels, 2 KB per launch (about one launch per 9 matrices), so no host
+ * memory is referenced after the call returns.
  *
  * Errors: every call validates all of its arguments before it enqueues
  * anything.  Any status other than MUON_ERR_HIP means nothing was enqueued.
@@ -117,7 +118,11 @@ typedef struct {
  *   coeffs: NULL = (3.4445, -4.7750, 2.0315) for every iteration; otherwise a
  *           HOST array of 3*ns_steps floats (a, b, c per iteration), read
  *           during the call only.
- *   ns_dtype: MUON_BF16 (bf16 operands, fp32 accumulation) or MUON_F32. */
+ *   ns_dtype: MUON_BF16 (bf16 operands, fp32 accumulation) or MUON_F32.
+ *           With MUON_BF16, a matrix whose short side is at most 32 still runs
+ *           the iteration in fp32: with that few singular values the bf16
+ *           rounding errors do not average out, and the result would miss the
+ *           bf16 iteration's usual accuracy on some inputs. */
 typedef struct {
     float lr;
     float momentum;     /* mu, typically 0.95 */
@@ -254,6 +259,15 @@ muon_status muon_test_poly_bf16(muon_handle h, const void* A, void* B, int64_t m
 muon_status muon_test_update_bf16(muon_handle h, const void* X, const void* B,
                                   void* Xo, int64_t m, int64_t n, int64_t ldx,
                                   int64_t ldb, float s, void* stream);
+
+/* Test hook of the scheduler: indices into `mats` (ascending, no repeats) of
+ * the matrices that hold a tile at which a grouped bf16 GEMM launch's per-XCD
+ * tile range starts or ends, or that hold quarter tiles (a short last round
+ * of 256-wide tiles split four ways).  Tests pick these matrices to check the
+ * tile indexing where it changes.  Writes min(cap, found) indices to `out`
+ * and the number found to *count.  Same validation as muon_workspace_size. */
+muon_status muon_test_split_matrices(muon_handle h, const muon_matrix* mats, int n,
+                                     const muon_hparams* hp, int32_t* out, int cap, int* count);
 
 #ifdef __cplusplus
 }

@@ -45,6 +45,7 @@ from ._lib import (  # noqa: F401
     muon_test_gram_bf16,
     muon_test_poly_bf16,
     muon_test_update_bf16,
+    muon_test_split_matrices,
     muon_workspace_size,
 )
 from .route import route_parameters  # noqa: F401

@@ -34,6 +34,7 @@ SYMBOLS = (
     "muon_profile_collect",
     "adamw_workspace_size",
     "adamw_step_clipped",
+    "muon_test_split_matrices",
 )
 
 NUM_PHASES = 7
@@ -137,12 +138,16 @@ def load():
                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.adamw_step_clipped.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
                                        ctypes.POINTER(AdamwHparams), f32, vp, vp, ctypes.c_size_t, vp]
+    lib.muon_test_split_matrices.argtypes = [vp, ctypes.POINTER(MuonMatrix), i32,
+                                             ctypes.POINTER(MuonHparams),
+                                             ctypes.POINTER(ctypes.c_int32), i32,
+                                             ctypes.POINTER(ctypes.c_int)]
     lib.muon_profile_enable.argtypes = [vp, i32]
     lib.muon_profile_collect.argtypes = [vp, ctypes.POINTER(PhaseTimes)]
     for name in ("muon_init", "muon_destroy", "muon_workspace_size", "muon_step_batched",
                  "adamw_step", "muon_test_gram_bf16", "muon_test_poly_bf16",
                  "muon_test_update_bf16", "muon_profile_enable", "muon_profile_collect",
-                 "adamw_workspace_size", "adamw_step_clipped"):
+                 "adamw_workspace_size", "adamw_step_clipped", "muon_test_split_matrices"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -331,6 +336,19 @@ def muon_test_update_bf16(h, X, B, Xo, m, n, ldx, ldb, s=1.0, stream=None):
     """Xo = s B X (bf16; X, Xo m x n with leading dimension ldx, B m x m)."""
     _check(load().muon_test_update_bf16(h, X.data_ptr(), B.data_ptr(), Xo.data_ptr(), m, n, ldx,
                                         ldb, s, _stream_ptr(stream)), "muon_test_update_bf16")
+
+
+def muon_test_split_matrices(h, mats, hp):
+    """Indices of the matrices whose tiles sit where the grouped GEMM
+    launches' per-XCD tile ranges start or end, or that hold quarter tiles."""
+    arr = _array(mats)
+    cnt = ctypes.c_int()
+    _check(load().muon_test_split_matrices(h, arr, len(mats), ctypes.byref(hp), None, 0,
+                                           ctypes.byref(cnt)), "muon_test_split_matrices")
+    out = (ctypes.c_int32 * max(cnt.value, 1))()
+    _check(load().muon_test_split_matrices(h, arr, len(mats), ctypes.byref(hp), out, cnt.value,
+                                           ctypes.byref(cnt)), "muon_test_split_matrices")
+    return list(out[:cnt.value])
 
 
 def muon_profile_enable(h, enable=True):

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-SOURCES = ["api.hip", "elementwise.hip", "gemm_bf16.hip", "gemm_f32.hip"]
+SOURCES = ["api.hip", "plan.cpp", "elementwise.hip", "gemm_bf16.hip", "gemm_f32.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,14 +1,15 @@
-// C ABI of libmuon: validation, workspace planning, descriptor upload and the
-// launch sequence of one Muon step; the AdamW entry point.
+// C ABI of libmuon: the launch sequence of one Muon step (planning is in
+// plan.cpp), the AdamW entry points, timing and the test hooks.
 //
 // One call of muon_step_batched enqueues, on the caller's stream:
-//   the descriptor-table upload (kernel arguments -> workspace, 2 KB a launch),
-//   momentum (one launch per elementwise tile kind in use), norm finalize,
-//   ns_steps x {gram, poly, update} (one grouped launch per size class in use),
-//   apply (one launch per elementwise tile kind in use).
-// The launch count does not depend on the number of matrices.  Matrices are
-// ordered by descending Newton-Schulz work in the table so the biggest tiles
-// are dispatched first.
+//   the descriptor-table upload: ceil(table bytes / 2 KB) launches; the table
+//     holds one 216-byte descriptor per matrix plus the prefix arrays, so
+//     about one launch per 9 matrices;
+//   momentum: one launch per elementwise tile kind in use (at most 3);
+//   norm finalize: one launch;
+//   ns_steps x {gram, poly, update}: one grouped launch per size class in use
+//     (at most 3) and phase;
+//   apply: one launch per elementwise tile kind in use.
 #include <math.h>
 #include <string.h>
 
@@ -18,6 +19,7 @@
 #include <vector>
 
 #include "muon_internal.h"
+#include "plan.h"
 
 using namespace muon;
 
@@ -57,279 +59,11 @@ struct DeviceGuard {
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline int64_t pad_to(int64_t v, int64_t p) { return (v + p - 1) / p * p; }
 
 bool finite(float v) { return isfinite(v) != 0; }
 
 size_t elem_bytes(int32_t dt) { return dt == MUON_BF16 ? 2 : 4; }
 bool valid_dtype(int32_t dt) { return dt == MUON_F32 || dt == MUON_BF16; }
-
-struct Range {
-    uintptr_t lo, hi;
-};
-Range span_of(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es) {
-    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
-    return Range{b, b + (size_t)((rows - 1) * ld + cols) * es};
-}
-bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
-
-double shape_multiplier(int mode, int64_t rows, int64_t cols) {
-    const double r = (double)rows, c = (double)cols;
-    switch (mode) {
-        case MUON_SCALE_MOONLIGHT: return 0.2 * sqrt(r > c ? r : c);
-        case MUON_SCALE_JORDAN: return sqrt(r / c > 1.0 ? r / c : 1.0);
-        case MUON_SCALE_BERNSTEIN: return sqrt(r / c);
-        default: return 1.0;
-    }
-}
-
-muon_status check_hparams(const muon_hparams* hp) {
-    if (!hp) return MUON_ERR_INVALID_ARG;
-    if (hp->ns_steps < 1 || hp->ns_steps > 1000) return MUON_ERR_INVALID_ARG;
-    if (!valid_dtype(hp->ns_dtype)) return MUON_ERR_INVALID_ARG;
-    if (hp->scale_mode < MUON_SCALE_MOONLIGHT || hp->scale_mode > MUON_SCALE_NONE)
-        return MUON_ERR_INVALID_ARG;
-    if (hp->nesterov != 0 && hp->nesterov != 1) return MUON_ERR_INVALID_ARG;
-    if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) ||
-        !finite(hp->eps) || !finite(hp->extra_scale))
-        return MUON_ERR_INVALID_ARG;
-    if (hp->eps < 0.f) return MUON_ERR_INVALID_ARG;
-    if (!finite(hp->qk_tau) || hp->qk_tau < 0.f) return MUON_ERR_INVALID_ARG;
-    if (hp->coeffs) {
-        for (int i = 0; i < 3 * hp->ns_steps; ++i)
-            if (!finite(hp->coeffs[i])) return MUON_ERR_INVALID_ARG;
-    }
-    return MUON_OK;
-}
-
-constexpr int64_t kMaxDim = 1 << 20;
-static_assert(kSmallBf16 % kTrTH == 0 && kSmallBf16 % kTrTW == 0,
-              "transposing elementwise tiles must divide every bf16 padding");
-static_assert(kPadF32 % kEwTile == 0, "fp32 elementwise tiles must divide the fp32 padding");
-
-muon_status check_matrix(const muon_matrix& m, bool need_ptrs) {
-    if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return MUON_ERR_INVALID_ARG;
-    if (m.ld_param < m.cols || m.ld_grad < m.cols || m.ld_mom < m.cols) return MUON_ERR_INVALID_ARG;
-    if (!valid_dtype(m.param_dtype) || !valid_dtype(m.grad_dtype)) return MUON_ERR_INVALID_ARG;
-    if (!need_ptrs) return MUON_OK;
-    if (!m.param || !m.grad || !m.momentum) return MUON_ERR_INVALID_ARG;
-    if (m.qk_smax && (m.qk_block_rows < 1 || m.qk_block_rows > m.rows)) return MUON_ERR_INVALID_ARG;
-    if (m.qk_smax && reinterpret_cast<uintptr_t>(m.qk_smax) % 4) return MUON_ERR_UNALIGNED;
-    const size_t pes = elem_bytes(m.param_dtype), ges = elem_bytes(m.grad_dtype);
-    if (reinterpret_cast<uintptr_t>(m.param) % pes || reinterpret_cast<uintptr_t>(m.grad) % ges ||
-        reinterpret_cast<uintptr_t>(m.momentum) % 4 ||
-        (m.update_out && reinterpret_cast<uintptr_t>(m.update_out) % 4) ||
-        (m.norm_out && reinterpret_cast<uintptr_t>(m.norm_out) % 4))
-        return MUON_ERR_UNALIGNED;
-    const Range rp = span_of(m.param, m.rows, m.cols, m.ld_param, pes);
-    const Range rg = span_of(m.grad, m.rows, m.cols, m.ld_grad, ges);
-    const Range rm = span_of(m.momentum, m.rows, m.cols, m.ld_mom, 4);
-    if (overlaps(rp, rg) || overlaps(rp, rm) || overlaps(rg, rm)) return MUON_ERR_OVERLAP;
-    if (m.update_out) {
-        const Range ru = span_of(m.update_out, m.rows, m.cols, m.cols, 4);
-        if (overlaps(ru, rp) || overlaps(ru, rg) || overlaps(ru, rm)) return MUON_ERR_OVERLAP;
-    }
-    return MUON_OK;
-}
-
-bool aligned_rows(const void* p, int64_t ld, size_t es) {
-    const size_t vec_bytes = 4 * es;
-    return reinterpret_cast<uintptr_t>(p) % vec_bytes == 0 && ld % 4 == 0;
-}
-
-// Workspace plan for one call.  Matrices are split into two classes with
-// their own GEMM tile size: "large" (256-wide tiles and padding) and, for
-// bf16 Newton-Schulz, "small" (short side <= 128: 128-wide tiles and
-// padding).  The descriptor table holds the large class first; each class has
-// its own prefix arrays of Gram/polynomial and update tiles.  The elementwise
-// kernels run over all matrices, one launch per tile kind (streaming, or
-// through LDS), each with a prefix array of its own.
-struct ClassPlan {
-    int first = 0, count = 0;           // descriptor range
-    std::vector<int32_t> pgram, pupd;   // count + 1 entries each
-    size_t off_pgram = 0, off_pupd = 0;
-    int total_gram = 0, total_upd = 0;
-    XcdSplit xs_gram, xs_poly, xs_upd;  // per-XCD tile ranges of equal work
-};
-
-struct Plan {
-    std::vector<MatDesc> d;
-    std::vector<int32_t> pew;        // elementwise tiles of all kinds (norm partial offsets)
-    std::vector<int32_t> pek[2];     // elementwise tiles by kind (launch prefixes)
-    ClassPlan cls[2];  // 0 large, 1 small
-    size_t off_pek[2] = {0, 0}, table_bytes = 0;
-    size_t off_partials = 0, off_invnorm = 0, total = 0;
-    int total_ek[2] = {0, 0};
-    int ns_f32 = 0;
-};
-
-muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
-                      uintptr_t ws, int cus, Plan& P) {
-    if (!mats || n < 1) return MUON_ERR_INVALID_ARG;
-    muon_status st = check_hparams(hp);
-    if (st != MUON_OK) return st;
-    for (int i = 0; i < n; ++i) {
-        st = check_matrix(mats[i], need_ptrs);
-        if (st != MUON_OK) return st;
-    }
-    P.ns_f32 = hp->ns_dtype == MUON_F32;
-    const size_t es = P.ns_f32 ? 4 : 2;
-    auto is_small = [&](int i) {
-        return !P.ns_f32 && std::min(mats[i].rows, mats[i].cols) <= kSmallBf16;
-    };
-
-    // order: large class first, each class by descending Newton-Schulz work
-    std::vector<int> order(n);
-    std::iota(order.begin(), order.end(), 0);
-    auto work = [&](int i) {
-        const double m = (double)std::min(mats[i].rows, mats[i].cols);
-        const double nn = (double)std::max(mats[i].rows, mats[i].cols);
-        return m * m * nn;
-    };
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-        if (is_small(a) != is_small(b)) return !is_small(a);
-        return work(a) > work(b);
-    });
-
-    P.d.assign(n, MatDesc{});
-    P.pew.assign(n + 1, 0);
-    P.pek[0].assign(n + 1, 0);
-    P.pek[1].assign(n + 1, 0);
-    int64_t tew = 0, tek[2] = {0, 0};
-    int nsmall = 0;
-    for (int i = 0; i < n; ++i) nsmall += is_small(i) ? 1 : 0;
-    P.cls[0].first = 0;
-    P.cls[0].count = n - nsmall;
-    P.cls[1].first = n - nsmall;
-    P.cls[1].count = nsmall;
-    for (int c = 0; c < 2; ++c) {
-        P.cls[c].pgram.assign(P.cls[c].count + 1, 0);
-        P.cls[c].pupd.assign(P.cls[c].count + 1, 0);
-    }
-    int64_t tgram[2] = {0, 0}, tupd[2] = {0, 0};
-    for (int k = 0; k < n; ++k) {
-        const muon_matrix& m = mats[order[k]];
-        const int c = k < P.cls[1].first ? 0 : 1;
-        const int64_t pad = P.ns_f32 ? kPadF32 : (c ? kSmallBf16 : kPadBf16);
-        const int symT = P.ns_f32 ? kTileF32 : gemm_tile_bf16(c);
-        const int updM = P.ns_f32 ? kTileF32 : upd_tile_m_bf16(c);
-        const int updN = P.ns_f32 ? kTileF32 : upd_tile_n_bf16(c);
-        MatDesc& d = P.d[k];
-        d.param = m.param;
-        d.grad = m.grad;
-        d.mom = m.momentum;
-        d.update_out = m.update_out;
-        d.norm_out = m.norm_out;
-        d.qk_smax = m.qk_smax;
-        d.qk_block_rows = m.qk_smax ? m.qk_block_rows : 0;
-        d.rows = m.rows;
-        d.cols = m.cols;
-        d.ld_param = m.ld_param;
-        d.ld_grad = m.ld_grad;
-        d.ld_mom = m.ld_mom;
-        d.param_dtype = m.param_dtype;
-        d.grad_dtype = m.grad_dtype;
-        d.transposed = m.rows > m.cols ? 1 : 0;
-        d.rows_pad = (int32_t)pad_to(m.rows, pad);
-        d.cols_pad = (int32_t)pad_to(m.cols, pad);
-        d.mp = d.transposed ? d.cols_pad : d.rows_pad;
-        d.np = d.transposed ? d.rows_pad : d.cols_pad;
-        // 16 x 256 streaming tiles unless Y is also needed transposed (the
-        // fp32 iteration keeps X^T; bf16 writes Y^T when rows > cols)
-        if (P.ns_f32) {
-            d.ew_th = d.ew_tw = kEwTile;
-        } else if (!d.transposed && d.cols_pad % 256 == 0) {
-            d.ew_th = 16;
-            d.ew_tw = 256;
-        } else {
-            d.ew_th = kTrTH;
-            d.ew_tw = kTrTW;
-        }
-        d.ew_tiles_c = d.cols_pad / d.ew_tw;
-        d.ew_tiles = (d.rows_pad / d.ew_th) * d.ew_tiles_c;
-        d.vec4 = need_ptrs && m.cols % 4 == 0 &&
-                 aligned_rows(m.param, m.ld_param, elem_bytes(m.param_dtype)) &&
-                 aligned_rows(m.grad, m.ld_grad, elem_bytes(m.grad_dtype)) &&
-                 aligned_rows(m.momentum, m.ld_mom, 4);
-        d.scale = (float)(shape_multiplier(hp->scale_mode, m.rows, m.cols) * (double)hp->extra_scale);
-        const int64_t Ts = d.mp / symT;
-        const int64_t gram_tiles = P.ns_f32 ? Ts * Ts : Ts * (Ts + 1) / 2;
-        const int64_t upd_tiles = (d.mp / updM) * (d.np / updN);
-        tew += d.ew_tiles;
-        tek[d.ew_th == 16 ? 0 : 1] += d.ew_tiles;
-        tgram[c] += gram_tiles;
-        tupd[c] += upd_tiles;
-        if (tew > INT32_MAX || tgram[c] > INT32_MAX / 2 || tupd[c] > INT32_MAX / 2)
-            return MUON_ERR_INVALID_ARG;
-        P.pew[k + 1] = (int32_t)tew;
-        P.pek[0][k + 1] = (int32_t)tek[0];
-        P.pek[1][k + 1] = (int32_t)tek[1];
-        const int kc = k - P.cls[c].first;
-        P.cls[c].pgram[kc + 1] = (int32_t)tgram[c];
-        P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
-    }
-    P.total_ek[0] = (int)tek[0];
-    P.total_ek[1] = (int)tek[1];
-    for (int c = 0; c < 2; ++c) {
-        ClassPlan& C = P.cls[c];
-        C.total_gram = (int)tgram[c];
-        C.total_upd = (int)tupd[c];
-        // tile work = k-steps: the Gram runs over n', the polynomial and the
-        // update over m'
-        std::vector<int32_t> tg(C.count), tu(C.count);
-        std::vector<int64_t> wn(C.count), wm(C.count);
-        for (int k = 0; k < C.count; ++k) {
-            tg[k] = C.pgram[k + 1] - C.pgram[k];
-            tu[k] = C.pupd[k + 1] - C.pupd[k];
-            wn[k] = P.d[C.first + k].np;
-            wm[k] = P.d[C.first + k].mp;
-        }
-        // quarter tiles for the short last round: large bf16 class only
-        const int quarters = (!P.ns_f32 && c == 0) ? 1 : 0;
-        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count, cus, quarters);
-        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count, cus, quarters);
-        C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters);
-    }
-
-    size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
-    for (int kind = 0; kind < 2; ++kind) {
-        P.off_pek[kind] = off;
-        off = align_up(off + (size_t)(n + 1) * 4, 256);
-    }
-    for (int c = 0; c < 2; ++c) {
-        P.cls[c].off_pgram = off;
-        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
-        P.cls[c].off_pupd = off;
-        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
-    }
-    P.table_bytes = off;
-    P.off_partials = off;
-    off = align_up(off + (size_t)tew * 4, 256);
-    P.off_invnorm = off;
-    off = align_up(off + (size_t)n * 4, 256);
-    for (int k = 0; k < n; ++k) {
-        MatDesc& d = P.d[k];
-        const size_t xb = (size_t)d.mp * (size_t)d.np * es;
-        const size_t ab = (size_t)d.mp * (size_t)d.mp * es;
-        // X^T is kept only by the fp32 iteration; the bf16 update reads X
-        // k-major directly
-        d.xt[0] = d.xt[1] = nullptr;
-        void** bufs[4] = {&d.x[0], &d.x[1], &d.xt[0], &d.xt[1]};
-        const int nbufs = P.ns_f32 ? 4 : 2;
-        for (int i = 0; i < nbufs; ++i) {
-            *bufs[i] = reinterpret_cast<void*>(ws + off);
-            off = align_up(off + xb, 256);
-        }
-        d.a = reinterpret_cast<void*>(ws + off);
-        off = align_up(off + ab, 256);
-        d.b = reinterpret_cast<void*>(ws + off);
-        off = align_up(off + ab, 256);
-        d.partials = reinterpret_cast<float*>(ws + P.off_partials) + (P.pew[k]);
-        d.inv_norm = reinterpret_cast<float*>(ws + P.off_invnorm) + k;
-    }
-    P.total = off;
-    return MUON_OK;
-}
 
 muon_status hip_status(hipError_t e) { return e == hipSuccess ? MUON_OK : MUON_ERR_HIP; }
 
@@ -436,32 +170,23 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     // workspace in kernel arguments.  Nothing waits on the host and nothing
     // refers to host memory after the call, so the step can be captured in a
     // graph and replayed.
-    h->table.assign(P.table_bytes, 0);
-    char* hb = h->table.data();
-    memcpy(hb, P.d.data(), (size_t)n * sizeof(MatDesc));
-    for (int kind = 0; kind < 2; ++kind)
-        memcpy(hb + P.off_pek[kind], P.pek[kind].data(), (size_t)(n + 1) * 4);
-    for (const ClassPlan& c : P.cls) {
-        memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
-        memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
-    }
-    if (launch_table_upload(hb, P.table_bytes, workspace, s) != hipSuccess) return MUON_ERR_HIP;
+    table_image(P, h->table);
+    if (launch_table_upload(h->table.data(), P.table_bytes, workspace, s) != hipSuccess)
+        return MUON_ERR_HIP;
 
     const MatDesc* dd = reinterpret_cast<const MatDesc*>(workspace);
     EwGroups eg;  // elementwise kernels: all matrices, by tile kind
-    for (int kind = 0; kind < 2; ++kind) {
+    for (int kind = 0; kind < kNumEwKinds; ++kind) {
         eg.prefix[kind] = reinterpret_cast<const int32_t*>(ws + P.off_pek[kind]);
         eg.tiles[kind] = P.total_ek[kind];
     }
-    Prefix pc[2];
-    for (int c = 0; c < 2; ++c) {
+    Prefix pc[kNumClasses];
+    for (int c = 0; c < kNumClasses; ++c) {
         pc[c].gram = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pgram);
         pc[c].upd = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pupd);
     }
 
-    hipError_t e = timed(h, 0, s, [&] {
-        return launch_momentum(dd, n, eg, hp->momentum, hp->nesterov, P.ns_f32, s);
-    });
+    hipError_t e = timed(h, 0, s, [&] { return launch_momentum(dd, n, eg, hp->momentum, hp->nesterov, s); });
     if (e == hipSuccess) e = timed(h, 1, s, [&] { return launch_norm_finalize(dd, n, hp->eps, s); });
     for (int it = 0; it < hp->ns_steps && e == hipSuccess; ++it) {
         float a = kMuonA, b = kMuonB, c = kMuonC;
@@ -470,39 +195,38 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             b = hp->coeffs[3 * it + 1];
             c = hp->coeffs[3 * it + 2];
         }
-        if (P.ns_f32) {
-            const ClassPlan& L = P.cls[0];
-            e = timed(h, 2, s, [&] { return launch_gram_f32(dd, L.count, pc[0], L.total_gram, it, s); });
-            if (e == hipSuccess)
-                e = timed(h, 3, s, [&] { return launch_poly_f32(dd, L.count, pc[0], L.total_gram, b, c, s); });
-            if (e == hipSuccess)
-                e = timed(h, 4, s, [&] { return launch_update_f32(dd, L.count, pc[0], L.total_upd, it, a, s); });
-            continue;
-        }
-        // the two classes' launches of one phase are independent of each other
-        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        // the classes' launches of one phase are independent of each other
+        for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 2, s, [&] { return launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k, s); });
+            e = timed(h, 2, s, [&] {
+                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, s)
+                                 : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall, s);
+            });
         }
-        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 3, s, [&] { return launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, a, b, c, k, s); });
+            e = timed(h, 3, s, [&] {
+                return k == kF32 ? launch_poly_f32(dc, C.count, pc[k], C.total_gram, b, c, s)
+                                 : launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, a, b, c, k == kSmall, s);
+            });
         }
-        for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+        for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 4, s, [&] { return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k, s); });
+            e = timed(h, 4, s, [&] {
+                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, a, s)
+                                 : launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, s);
+            });
         }
     }
     if (e == hipSuccess)
         e = timed(h, 5, s, [&] {
-            return launch_apply(dd, n, eg, hp->ns_steps & 1, hp->lr, hp->weight_decay,
-                                hp->qk_tau, P.ns_f32, s);
+            return launch_apply(dd, n, eg, hp->ns_steps & 1, hp->lr, hp->weight_decay, hp->qk_tau, s);
         });
     return hip_status(e);
 }
@@ -676,9 +400,20 @@ muon_status muon_profile_collect(muon_handle h, muon_phase_times* out) {
 
 static muon_status check_single(muon_handle h, int64_t m, int64_t n) {
     if (!h) return MUON_ERR_INVALID_ARG;
-    const int T = gemm_tile_bf16(0);
+    const int T = kClassTile[kLarge];
     if (m < T || n < T || m % T || n % T || m > kMaxDim || n > kMaxDim) return MUON_ERR_INVALID_ARG;
-    if (upd_tile_m_bf16(0) != T || n % upd_tile_n_bf16(0)) return MUON_ERR_INVALID_ARG;
+    return MUON_OK;
+}
+
+muon_status muon_test_split_matrices(muon_handle h, const muon_matrix* mats, int n,
+                                     const muon_hparams* hp, int32_t* out, int cap, int* count) {
+    if (!h || !count || cap < 0 || (cap > 0 && !out)) return MUON_ERR_INVALID_ARG;
+    Plan P;
+    muon_status st = make_plan(mats, n, hp, false, 0, h->cus_per_xcd, P);
+    if (st != MUON_OK) return st;
+    const std::vector<int> idx = split_matrices(P);
+    *count = (int)idx.size();
+    for (int i = 0; i < cap && i < (int)idx.size(); ++i) out[i] = idx[i];
     return MUON_OK;
 }
 

@@ -605,15 +605,13 @@ hipError_t launch_clip_finalize(const float* partials, int nblocks, float max_no
 }
 
 hipError_t launch_momentum(const MatDesc* d, int n, const EwGroups& g, float mu, int nesterov,
-                           int ns_f32, hipStream_t st) {
-    if (g.tiles[0] > 0)  // streaming tiles occur only with the bf16 iteration
-        momentum_kernel<false, false><<<g.tiles[0], 256, 0, st>>>(d, n, g.prefix[0], mu, nesterov);
-    if (g.tiles[1] > 0) {
-        if (ns_f32)
-            momentum_kernel<true, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], mu, nesterov);
-        else
-            momentum_kernel<false, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], mu, nesterov);
-    }
+                           hipStream_t st) {
+    if (g.tiles[kEwStream] > 0)
+        momentum_kernel<false, false><<<g.tiles[kEwStream], 256, 0, st>>>(d, n, g.prefix[kEwStream], mu, nesterov);
+    if (g.tiles[kEwTrans] > 0)
+        momentum_kernel<false, true><<<g.tiles[kEwTrans], 256, 0, st>>>(d, n, g.prefix[kEwTrans], mu, nesterov);
+    if (g.tiles[kEwF32] > 0)
+        momentum_kernel<true, true><<<g.tiles[kEwF32], 256, 0, st>>>(d, n, g.prefix[kEwF32], mu, nesterov);
     return hipGetLastError();
 }
 
@@ -623,19 +621,17 @@ hipError_t launch_norm_finalize(const MatDesc* d, int n, float eps, hipStream_t 
 }
 
 hipError_t launch_apply(const MatDesc* d, int n, const EwGroups& g, int final_parity, float lr,
-                        float wd, float qk_tau, int ns_f32, hipStream_t st) {
+                        float wd, float qk_tau, hipStream_t st) {
     const float decay = 1.f - lr * wd;
-    if (g.tiles[0] > 0)
-        apply_kernel<false, false><<<g.tiles[0], 256, 0, st>>>(d, n, g.prefix[0], final_parity,
-                                                              decay, lr, qk_tau);
-    if (g.tiles[1] > 0) {
-        if (ns_f32)
-            apply_kernel<true, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], final_parity,
-                                                                decay, lr, qk_tau);
-        else
-            apply_kernel<false, true><<<g.tiles[1], 256, 0, st>>>(d, n, g.prefix[1], final_parity,
-                                                                 decay, lr, qk_tau);
-    }
+    if (g.tiles[kEwStream] > 0)
+        apply_kernel<false, false><<<g.tiles[kEwStream], 256, 0, st>>>(d, n, g.prefix[kEwStream],
+                                                                      final_parity, decay, lr, qk_tau);
+    if (g.tiles[kEwTrans] > 0)
+        apply_kernel<false, true><<<g.tiles[kEwTrans], 256, 0, st>>>(d, n, g.prefix[kEwTrans],
+                                                                    final_parity, decay, lr, qk_tau);
+    if (g.tiles[kEwF32] > 0)
+        apply_kernel<true, true><<<g.tiles[kEwF32], 256, 0, st>>>(d, n, g.prefix[kEwF32],
+                                                                 final_parity, decay, lr, qk_tau);
     return hipGetLastError();
 }
 

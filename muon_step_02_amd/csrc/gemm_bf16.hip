@@ -728,48 +728,11 @@ using SmallCfg = Cfg<128, 128, 2, 2>;
 
 }  // namespace
 
-int gemm_tile_bf16(int small) { return small ? SmallCfg::BM : SymCfg::BM; }
-int upd_tile_m_bf16(int small) { return small ? SmallCfg::BM : UpdCfg::BM; }
-int upd_tile_n_bf16(int small) { return small ? SmallCfg::BN : UpdCfg::BN; }
-
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters) {
-    XcdSplit xs;
-    int64_t total_w = 0, total_t = 0;
-    for (int k = 0; k < n; ++k) {
-        total_w += (int64_t)ntiles[k] * weight[k];
-        total_t += ntiles[k];
-    }
-    // boundary x: first tile whose preceding work reaches x/8 of the total
-    xs.b[0] = 0;
-    int x = 1;
-    int64_t cum_w = 0, cum_t = 0;
-    for (int k = 0; k < n && x < 8; ++k) {
-        const int64_t w = weight[k] > 0 ? weight[k] : 1;
-        const int64_t end_w = cum_w + (int64_t)ntiles[k] * w;
-        while (x < 8 && end_w * 8 >= (int64_t)x * total_w) {
-            // smallest t in [0, ntiles] with (cum_w + t*w) * 8 >= x * total_w
-            const int64_t need = (int64_t)x * total_w - cum_w * 8;
-            int64_t t = need <= 0 ? 0 : (need + 8 * w - 1) / (8 * w);
-            if (t > ntiles[k]) t = ntiles[k];
-            xs.b[x++] = (int32_t)(cum_t + t);
-        }
-        cum_w = end_w;
-        cum_t += ntiles[k];
-    }
-    while (x < 9) xs.b[x++] = (int32_t)total_t;
-    xs.b[8] = (int32_t)total_t;
-    xs.per = 0;
-    for (int i = 0; i < 8; ++i) {
-        if (xs.b[i + 1] < xs.b[i]) xs.b[i + 1] = xs.b[i];
-        const int T = xs.b[i + 1] - xs.b[i];
-        // last round of R tiles on `cus` CUs: as 4R quarter tiles when R <= cus/2
-        const int R = cus > 0 ? T % cus : 0;
-        xs.sub[i] = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
-        const int tasks = T + 3 * xs.sub[i];
-        if (tasks > xs.per) xs.per = tasks;
-    }
-    return xs;
-}
+static_assert(SymCfg::BM == kClassTile[kLarge] && UpdCfg::BM == kClassTile[kLarge] &&
+                  UpdCfg::BN == kClassTile[kLarge],
+              "256-class tiles");
+static_assert(SmallCfg::BM == kClassTile[kSmall] && SmallCfg::BN == kClassTile[kSmall],
+              "128-class tiles");
 
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                             int small, hipStream_t st) {

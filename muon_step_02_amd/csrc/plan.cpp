@@ -1,0 +1,381 @@
+// Host-side planning of one Muon step (see plan.h).
+#include "plan.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+
+// Bounds checks of the planner's own indexing: on in the sanitizer build of
+// this file, compiled out in the library.
+#ifdef MUON_PLAN_CHECKS
+#include <stdio.h>
+#include <stdlib.h>
+#define PLAN_CHECK(c)                                                           \
+    do {                                                                        \
+        if (!(c)) {                                                             \
+            fprintf(stderr, "plan check failed: %s (%s:%d)\n", #c, __FILE__, __LINE__); \
+            abort();                                                            \
+        }                                                                       \
+    } while (0)
+#else
+#define PLAN_CHECK(c) ((void)0)
+#endif
+
+namespace muon {
+
+namespace {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t pad_to(int64_t v, int64_t p) { return (v + p - 1) / p * p; }
+
+bool finite(float v) { return isfinite(v) != 0; }
+size_t elem_bytes(int32_t dt) { return dt == MUON_BF16 ? 2 : 4; }
+bool valid_dtype(int32_t dt) { return dt == MUON_F32 || dt == MUON_BF16; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+Range span_of(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Range{b, b + (size_t)((rows - 1) * ld + cols) * es};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+muon_status check_hparams(const muon_hparams* hp) {
+    if (!hp) return MUON_ERR_INVALID_ARG;
+    if (hp->ns_steps < 1 || hp->ns_steps > 1000) return MUON_ERR_INVALID_ARG;
+    if (!valid_dtype(hp->ns_dtype)) return MUON_ERR_INVALID_ARG;
+    if (hp->scale_mode < MUON_SCALE_MOONLIGHT || hp->scale_mode > MUON_SCALE_NONE)
+        return MUON_ERR_INVALID_ARG;
+    if (hp->nesterov != 0 && hp->nesterov != 1) return MUON_ERR_INVALID_ARG;
+    if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) ||
+        !finite(hp->eps) || !finite(hp->extra_scale))
+        return MUON_ERR_INVALID_ARG;
+    if (hp->eps < 0.f) return MUON_ERR_INVALID_ARG;
+    if (!finite(hp->qk_tau) || hp->qk_tau < 0.f) return MUON_ERR_INVALID_ARG;
+    if (hp->coeffs) {
+        for (int i = 0; i < 3 * hp->ns_steps; ++i)
+            if (!finite(hp->coeffs[i])) return MUON_ERR_INVALID_ARG;
+    }
+    return MUON_OK;
+}
+
+muon_status check_matrix(const muon_matrix& m, bool need_ptrs) {
+    if (m.rows < 1 || m.cols < 1 || m.rows > kMaxDim || m.cols > kMaxDim) return MUON_ERR_INVALID_ARG;
+    if (m.ld_param < m.cols || m.ld_grad < m.cols || m.ld_mom < m.cols) return MUON_ERR_INVALID_ARG;
+    if (!valid_dtype(m.param_dtype) || !valid_dtype(m.grad_dtype)) return MUON_ERR_INVALID_ARG;
+    if (!need_ptrs) return MUON_OK;
+    if (!m.param || !m.grad || !m.momentum) return MUON_ERR_INVALID_ARG;
+    if (m.qk_smax && (m.qk_block_rows < 1 || m.qk_block_rows > m.rows)) return MUON_ERR_INVALID_ARG;
+    if (m.qk_smax && reinterpret_cast<uintptr_t>(m.qk_smax) % 4) return MUON_ERR_UNALIGNED;
+    const size_t pes = elem_bytes(m.param_dtype), ges = elem_bytes(m.grad_dtype);
+    if (reinterpret_cast<uintptr_t>(m.param) % pes || reinterpret_cast<uintptr_t>(m.grad) % ges ||
+        reinterpret_cast<uintptr_t>(m.momentum) % 4 ||
+        (m.update_out && reinterpret_cast<uintptr_t>(m.update_out) % 4) ||
+        (m.norm_out && reinterpret_cast<uintptr_t>(m.norm_out) % 4))
+        return MUON_ERR_UNALIGNED;
+    const Range rp = span_of(m.param, m.rows, m.cols, m.ld_param, pes);
+    const Range rg = span_of(m.grad, m.rows, m.cols, m.ld_grad, ges);
+    const Range rm = span_of(m.momentum, m.rows, m.cols, m.ld_mom, 4);
+    if (overlaps(rp, rg) || overlaps(rp, rm) || overlaps(rg, rm)) return MUON_ERR_OVERLAP;
+    if (m.update_out) {
+        const Range ru = span_of(m.update_out, m.rows, m.cols, m.cols, 4);
+        if (overlaps(ru, rp) || overlaps(ru, rg) || overlaps(ru, rm)) return MUON_ERR_OVERLAP;
+    }
+    return MUON_OK;
+}
+
+bool aligned_rows(const void* p, int64_t ld, size_t es) {
+    const size_t vec_bytes = 4 * es;
+    return reinterpret_cast<uintptr_t>(p) % vec_bytes == 0 && ld % 4 == 0;
+}
+
+int size_class(const muon_matrix& m, bool ns_f32) {
+    const int64_t s = std::min(m.rows, m.cols);
+    if (ns_f32 || s <= kTinyF32) return kF32;
+    return s <= kSmallBf16 ? kSmall : kLarge;
+}
+
+// index k of the largest prefix[k] <= t (prefix[0] = 0 <= t < prefix[count])
+int owner(const std::vector<int32_t>& prefix, int32_t t) {
+    PLAN_CHECK(!prefix.empty() && prefix.front() <= t && t < prefix.back());
+    return (int)(std::upper_bound(prefix.begin(), prefix.end(), t) - prefix.begin()) - 1;
+}
+
+}  // namespace
+
+double shape_multiplier(int mode, int64_t rows, int64_t cols) {
+    const double r = (double)rows, c = (double)cols;
+    switch (mode) {
+        case MUON_SCALE_MOONLIGHT: return 0.2 * sqrt(r > c ? r : c);
+        case MUON_SCALE_JORDAN: return sqrt(r / c > 1.0 ? r / c : 1.0);
+        case MUON_SCALE_BERNSTEIN: return sqrt(r / c);
+        default: return 1.0;
+    }
+}
+
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters) {
+    XcdSplit xs;
+    int64_t total_w = 0, total_t = 0;
+    for (int k = 0; k < n; ++k) {
+        const int64_t w = weight[k] > 0 ? weight[k] : 1;
+        total_w += (int64_t)ntiles[k] * w;
+        total_t += ntiles[k];
+    }
+    // boundary x: first tile whose preceding work reaches x/8 of the total
+    xs.b[0] = 0;
+    int x = 1;
+    int64_t cum_w = 0, cum_t = 0;
+    for (int k = 0; k < n && x < 8; ++k) {
+        const int64_t w = weight[k] > 0 ? weight[k] : 1;
+        const int64_t end_w = cum_w + (int64_t)ntiles[k] * w;
+        while (x < 8 && end_w * 8 >= (int64_t)x * total_w) {
+            // smallest t in [0, ntiles] with (cum_w + t*w) * 8 >= x * total_w
+            const int64_t need = (int64_t)x * total_w - cum_w * 8;
+            int64_t t = need <= 0 ? 0 : (need + 8 * w - 1) / (8 * w);
+            if (t > ntiles[k]) t = ntiles[k];
+            PLAN_CHECK(x >= 1 && x < 9);
+            xs.b[x++] = (int32_t)(cum_t + t);
+        }
+        cum_w = end_w;
+        cum_t += ntiles[k];
+    }
+    while (x < 9) xs.b[x++] = (int32_t)total_t;
+    xs.b[8] = (int32_t)total_t;
+    xs.per = 0;
+    for (int i = 0; i < 8; ++i) {
+        if (xs.b[i + 1] < xs.b[i]) xs.b[i + 1] = xs.b[i];
+        const int T = xs.b[i + 1] - xs.b[i];
+        // last round of R tiles on `cus` CUs: as 4R quarter tiles when R <= cus/2
+        const int R = cus > 0 ? T % cus : 0;
+        xs.sub[i] = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
+        const int tasks = T + 3 * xs.sub[i];
+        if (tasks > xs.per) xs.per = tasks;
+    }
+    return xs;
+}
+
+// Workspace plan for one call.  Matrices are split into the size classes of
+// layout.h, each with its own GEMM tile and padding and its own prefix arrays
+// of Gram/polynomial and update tiles; the descriptor table holds kLarge
+// first, then kSmall, then kF32, each by descending Newton-Schulz work, so
+// the longest tiles are dispatched first.  The elementwise kernels run over
+// all matrices, one launch per tile kind, each with a prefix array of its own.
+muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
+                      uintptr_t ws, int cus, Plan& P) {
+    if (!mats || n < 1) return MUON_ERR_INVALID_ARG;
+    muon_status st = check_hparams(hp);
+    if (st != MUON_OK) return st;
+    for (int i = 0; i < n; ++i) {
+        st = check_matrix(mats[i], need_ptrs);
+        if (st != MUON_OK) return st;
+    }
+    const bool ns_f32 = hp->ns_dtype == MUON_F32;
+
+    std::vector<int> cls_of(n);
+    int count[kNumClasses] = {0, 0, 0};
+    for (int i = 0; i < n; ++i) {
+        cls_of[i] = size_class(mats[i], ns_f32);
+        ++count[cls_of[i]];
+    }
+    auto work = [&](int i) {
+        const double m = (double)std::min(mats[i].rows, mats[i].cols);
+        const double nn = (double)std::max(mats[i].rows, mats[i].cols);
+        return m * m * nn;
+    };
+    P.order.resize(n);
+    std::iota(P.order.begin(), P.order.end(), 0);
+    std::stable_sort(P.order.begin(), P.order.end(), [&](int a, int b) {
+        if (cls_of[a] != cls_of[b]) return cls_of[a] < cls_of[b];
+        return work(a) > work(b);
+    });
+
+    P.d.assign(n, MatDesc{});
+    P.pew.assign(n + 1, 0);
+    for (int kind = 0; kind < kNumEwKinds; ++kind) P.pek[kind].assign(n + 1, 0);
+    int first = 0;
+    for (int c = 0; c < kNumClasses; ++c) {
+        ClassPlan& C = P.cls[c];
+        C.first = first;
+        C.count = count[c];
+        first += count[c];
+        C.pgram.assign(C.count + 1, 0);
+        C.pupd.assign(C.count + 1, 0);
+    }
+    int64_t tew = 0, tek[kNumEwKinds] = {0, 0, 0};
+    int64_t tgram[kNumClasses] = {0, 0, 0}, tupd[kNumClasses] = {0, 0, 0};
+    for (int k = 0; k < n; ++k) {
+        const muon_matrix& m = mats[P.order[k]];
+        const int c = cls_of[P.order[k]];
+        PLAN_CHECK(k >= P.cls[c].first && k < P.cls[c].first + P.cls[c].count);
+        const int64_t pad = kClassPad[c];
+        const int64_t tile = kClassTile[c];
+        MatDesc& d = P.d[k];
+        d.param = m.param;
+        d.grad = m.grad;
+        d.mom = m.momentum;
+        d.update_out = m.update_out;
+        d.norm_out = m.norm_out;
+        d.qk_smax = m.qk_smax;
+        d.qk_block_rows = m.qk_smax ? m.qk_block_rows : 0;
+        d.rows = m.rows;
+        d.cols = m.cols;
+        d.ld_param = m.ld_param;
+        d.ld_grad = m.ld_grad;
+        d.ld_mom = m.ld_mom;
+        d.param_dtype = m.param_dtype;
+        d.grad_dtype = m.grad_dtype;
+        d.cls = c;
+        d.transposed = m.rows > m.cols ? 1 : 0;
+        d.rows_pad = (int32_t)pad_to(m.rows, pad);
+        d.cols_pad = (int32_t)pad_to(m.cols, pad);
+        d.mp = d.transposed ? d.cols_pad : d.rows_pad;
+        d.np = d.transposed ? d.rows_pad : d.cols_pad;
+        int kind;
+        if (c == kF32) {
+            kind = kEwF32;
+            d.ew_th = d.ew_tw = kEwTile;
+        } else if (!d.transposed && d.cols_pad % 256 == 0) {
+            // the bf16 iteration reads Y as it is: streaming tiles
+            kind = kEwStream;
+            d.ew_th = 16;
+            d.ew_tw = 256;
+        } else {
+            kind = kEwTrans;
+            d.ew_th = kTrTH;
+            d.ew_tw = kTrTW;
+        }
+        PLAN_CHECK(d.rows_pad % d.ew_th == 0 && d.cols_pad % d.ew_tw == 0);
+        d.ew_tiles_c = d.cols_pad / d.ew_tw;
+        d.ew_tiles = (d.rows_pad / d.ew_th) * d.ew_tiles_c;
+        d.vec4 = need_ptrs && m.cols % 4 == 0 &&
+                 aligned_rows(m.param, m.ld_param, elem_bytes(m.param_dtype)) &&
+                 aligned_rows(m.grad, m.ld_grad, elem_bytes(m.grad_dtype)) &&
+                 aligned_rows(m.momentum, m.ld_mom, 4);
+        d.scale = (float)(shape_multiplier(hp->scale_mode, m.rows, m.cols) * (double)hp->extra_scale);
+        const int64_t Ts = d.mp / tile;
+        // the bf16 kernels compute the symmetric products on the lower
+        // triangle of tiles; the fp32 ones compute every tile
+        const int64_t gram_tiles = c == kF32 ? Ts * Ts : Ts * (Ts + 1) / 2;
+        const int64_t upd_tiles = (d.mp / tile) * (d.np / tile);
+        tew += d.ew_tiles;
+        tek[kind] += d.ew_tiles;
+        tgram[c] += gram_tiles;
+        tupd[c] += upd_tiles;
+        if (tew > INT32_MAX || tgram[c] > INT32_MAX / 2 || tupd[c] > INT32_MAX / 2)
+            return MUON_ERR_INVALID_ARG;
+        P.pew[k + 1] = (int32_t)tew;
+        for (int kk = 0; kk < kNumEwKinds; ++kk) P.pek[kk][k + 1] = (int32_t)tek[kk];
+        const int kc = k - P.cls[c].first;
+        P.cls[c].pgram[kc + 1] = (int32_t)tgram[c];
+        P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
+    }
+    for (int kind = 0; kind < kNumEwKinds; ++kind) P.total_ek[kind] = (int)tek[kind];
+    for (int c = 0; c < kNumClasses; ++c) {
+        ClassPlan& C = P.cls[c];
+        C.total_gram = (int)tgram[c];
+        C.total_upd = (int)tupd[c];
+        if (c == kF32 || C.count == 0) continue;
+        // tile work = k-steps: the Gram runs over n', the polynomial and the
+        // update over m'
+        std::vector<int32_t> tg(C.count), tu(C.count);
+        std::vector<int64_t> wn(C.count), wm(C.count);
+        for (int k = 0; k < C.count; ++k) {
+            tg[k] = C.pgram[k + 1] - C.pgram[k];
+            tu[k] = C.pupd[k + 1] - C.pupd[k];
+            wn[k] = P.d[C.first + k].np;
+            wm[k] = P.d[C.first + k].mp;
+        }
+        // quarter tiles for the short last round: 256-tile class only
+        const int quarters = c == kLarge ? 1 : 0;
+        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count, cus, quarters);
+        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count, cus, quarters);
+        C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters);
+    }
+
+    size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
+    for (int kind = 0; kind < kNumEwKinds; ++kind) {
+        P.off_pek[kind] = off;
+        off = align_up(off + (size_t)(n + 1) * 4, 256);
+    }
+    for (int c = 0; c < kNumClasses; ++c) {
+        P.cls[c].off_pgram = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+        P.cls[c].off_pupd = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+    }
+    P.table_bytes = off;
+    P.off_partials = off;
+    off = align_up(off + (size_t)tew * 4, 256);
+    P.off_invnorm = off;
+    off = align_up(off + (size_t)n * 4, 256);
+    for (int k = 0; k < n; ++k) {
+        MatDesc& d = P.d[k];
+        const size_t es = d.cls == kF32 ? 4 : 2;
+        const size_t xb = (size_t)d.mp * (size_t)d.np * es;
+        const size_t ab = (size_t)d.mp * (size_t)d.mp * es;
+        // X^T is kept only by the fp32 iteration; the bf16 update reads X
+        // k-major directly
+        d.xt[0] = d.xt[1] = nullptr;
+        void** bufs[4] = {&d.x[0], &d.x[1], &d.xt[0], &d.xt[1]};
+        const int nbufs = d.cls == kF32 ? 4 : 2;
+        for (int i = 0; i < nbufs; ++i) {
+            *bufs[i] = reinterpret_cast<void*>(ws + off);
+            off = align_up(off + xb, 256);
+        }
+        d.a = reinterpret_cast<void*>(ws + off);
+        off = align_up(off + ab, 256);
+        d.b = reinterpret_cast<void*>(ws + off);
+        off = align_up(off + ab, 256);
+        d.partials = reinterpret_cast<float*>(ws + P.off_partials) + P.pew[k];
+        d.inv_norm = reinterpret_cast<float*>(ws + P.off_invnorm) + k;
+    }
+    P.total = off;
+    return MUON_OK;
+}
+
+void table_image(const Plan& P, std::vector<char>& out) {
+    const int n = (int)P.d.size();
+    out.assign(P.table_bytes, 0);
+    char* hb = out.data();
+    PLAN_CHECK((size_t)n * sizeof(MatDesc) <= P.table_bytes);
+    memcpy(hb, P.d.data(), (size_t)n * sizeof(MatDesc));
+    for (int kind = 0; kind < kNumEwKinds; ++kind) {
+        PLAN_CHECK(P.off_pek[kind] + (size_t)(n + 1) * 4 <= P.table_bytes);
+        memcpy(hb + P.off_pek[kind], P.pek[kind].data(), (size_t)(n + 1) * 4);
+    }
+    for (const ClassPlan& c : P.cls) {
+        PLAN_CHECK(c.off_pgram + (size_t)(c.count + 1) * 4 <= P.table_bytes);
+        PLAN_CHECK(c.off_pupd + (size_t)(c.count + 1) * 4 <= P.table_bytes);
+        memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
+        memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
+    }
+}
+
+std::vector<int> split_matrices(const Plan& P) {
+    std::vector<int> out;
+    for (int c = kLarge; c <= kSmall; ++c) {
+        const ClassPlan& C = P.cls[c];
+        if (C.count == 0) continue;
+        const XcdSplit* splits[3] = {&C.xs_gram, &C.xs_poly, &C.xs_upd};
+        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.pgram, &C.pupd};
+        for (int s = 0; s < 3; ++s) {
+            const XcdSplit& xs = *splits[s];
+            const std::vector<int32_t>& pre = *prefixes[s];
+            auto mark = [&](int32_t t) { out.push_back(P.order[C.first + owner(pre, t)]); };
+            for (int x = 0; x < 8; ++x) {
+                if (xs.b[x] == xs.b[x + 1]) continue;
+                mark(xs.b[x]);
+                mark(xs.b[x + 1] - 1);
+                for (int32_t t = xs.b[x + 1] - xs.sub[x]; t < xs.b[x + 1]; ++t) mark(t);
+            }
+        }
+    }
+    std::sort(out.begin(), out.end());
+    out.erase(std::unique(out.begin(), out.end()), out.end());
+    return out;
+}
+
+}  // namespace muon

@@ -1,0 +1,59 @@
+// Host-side planning of one Muon step: validation, size classes, the order
+// of the descriptor table, tile prefixes, per-XCD tile ranges and the
+// workspace layout.  Plain C++ (no HIP), so that it is also built and checked
+// on its own under host sanitizers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/muon.h"
+#include "layout.h"
+
+namespace muon {
+
+// Tiles and launch ranges of one size class.
+struct ClassPlan {
+    int first = 0, count = 0;           // descriptor range [first, first + count)
+    std::vector<int32_t> pgram, pupd;   // count + 1 entries each
+    size_t off_pgram = 0, off_pupd = 0; // their offsets in the workspace
+    int total_gram = 0, total_upd = 0;
+    XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
+};
+
+struct Plan {
+    std::vector<MatDesc> d;          // descriptor table, in launch order
+    std::vector<int> order;          // d[k] describes the caller's matrix order[k]
+    std::vector<int32_t> pew;        // elementwise tiles of all kinds (norm partial offsets)
+    std::vector<int32_t> pek[kNumEwKinds];  // elementwise tiles by kind (launch prefixes)
+    ClassPlan cls[kNumClasses];
+    size_t off_pek[kNumEwKinds] = {};
+    size_t table_bytes = 0;          // descriptor table + prefixes, at the workspace start
+    size_t off_partials = 0, off_invnorm = 0, total = 0;
+    int total_ek[kNumEwKinds] = {};
+};
+
+// Everything about one call that does not touch the device.  `ws` is the
+// workspace address the descriptors point into (0 to size the workspace
+// only); `need_ptrs` checks the tensor pointers too (alignment, overlap);
+// `cus` is the number of compute units per XCD.  Any status other than
+// MUON_OK leaves P unspecified.
+muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
+                      uintptr_t ws, int cus, Plan& P);
+
+// Host image of the workspace's first P.table_bytes bytes: the descriptors
+// and every prefix array.
+void table_image(const Plan& P, std::vector<char>& out);
+
+// Caller indices (ascending, no repeats) of the matrices that hold a tile at
+// the start or end of a per-XCD range of a bf16 GEMM launch, or quarter tiles.
+std::vector<int> split_matrices(const Plan& P);
+
+// Per-matrix multiplier of the orthogonalised update (muon_scale_mode).
+double shape_multiplier(int mode, int64_t rows, int64_t cols);
+
+constexpr int64_t kMaxDim = 1 << 20;
+
+}  // namespace muon
