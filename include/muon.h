@@ -57,7 +57,8 @@ typedef enum {
     MUON_ERR_WORKSPACE = 3,          /* workspace null or smaller than required */
     MUON_ERR_OVERLAP = 4,            /* param/grad/momentum ranges overlap  */
     MUON_ERR_HIP = 5,                /* a HIP runtime call failed           */
-    MUON_ERR_UNALIGNED = 6           /* pointer not aligned to its element  */
+    MUON_ERR_UNALIGNED = 6,          /* pointer not aligned to its element  */
+    MUON_ERR_SCRATCH = 7             /* larger than the fixed scratch of an allocation-free call */
 } muon_status;
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
@@ -235,6 +236,25 @@ muon_status adamw_workspace_size(muon_handle h, const adamw_tensor* ts, int n, s
 muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
                                const adamw_hparams* hp, float max_norm, float* norm_out,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* adamw_step_clipped for callers that cannot allocate device memory: code
+ * under stream capture that may not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results and validation
+ * as adamw_step_clipped, without the workspace: the per-chunk partial sums
+ * and the clip scale live in a fixed device array that the library holds,
+ * one copy per device, for the life of the process (1 MiB + 256 bytes,
+ * resolved by muon_init).  The call itself allocates nothing.
+ * Limit: the tensors together may hold at most 2^18 chunks of 4096 elements
+ * (2^30 elements when every numel is a multiple of 4096; each tensor counts
+ * ceil(numel / 4096) chunks); beyond it the call returns MUON_ERR_SCRATCH
+ * and enqueues nothing.
+ * Every call on one device shares that array, which keeps the last call's
+ * contents (nothing in it needs to start at zero).  Calls that may overlap in
+ * time on one device -- on different streams, or through different handles
+ * of that device -- race on it and must not be made. */
+muon_status adamw_step_clipped_noalloc(muon_handle h, const adamw_tensor* ts, int n,
+                                       const adamw_hparams* hp, float max_norm,
+                                       float* norm_out, void* stream);
 
 /* Static, human readable name of a status. */
 const char* muon_status_str(muon_status s);

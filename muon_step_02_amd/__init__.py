@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     adamw_hparams,
     adamw_step,
     adamw_step_clipped,
+    adamw_step_clipped_noalloc,
     adamw_workspace_size,
     adamw_tensor,
     exported_symbols,

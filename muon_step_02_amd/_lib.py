@@ -17,6 +17,7 @@ STATUS = {
     4: "MUON_ERR_OVERLAP",
     5: "MUON_ERR_HIP",
     6: "MUON_ERR_UNALIGNED",
+    7: "MUON_ERR_SCRATCH",
 }
 
 # every entry point include/muon.h declares
@@ -35,6 +36,7 @@ SYMBOLS = (
     "adamw_workspace_size",
     "adamw_step_clipped",
     "muon_test_split_matrices",
+    "adamw_step_clipped_noalloc",
 )
 
 NUM_PHASES = 7
@@ -142,12 +144,15 @@ def load():
                                              ctypes.POINTER(MuonHparams),
                                              ctypes.POINTER(ctypes.c_int32), i32,
                                              ctypes.POINTER(ctypes.c_int)]
+    lib.adamw_step_clipped_noalloc.argtypes = [vp, ctypes.POINTER(AdamwTensor), i32,
+                                               ctypes.POINTER(AdamwHparams), f32, vp, vp]
     lib.muon_profile_enable.argtypes = [vp, i32]
     lib.muon_profile_collect.argtypes = [vp, ctypes.POINTER(PhaseTimes)]
     for name in ("muon_init", "muon_destroy", "muon_workspace_size", "muon_step_batched",
                  "adamw_step", "muon_test_gram_bf16", "muon_test_poly_bf16",
                  "muon_test_update_bf16", "muon_profile_enable", "muon_profile_collect",
-                 "adamw_workspace_size", "adamw_step_clipped", "muon_test_split_matrices"):
+                 "adamw_workspace_size", "adamw_step_clipped", "muon_test_split_matrices",
+                 "adamw_step_clipped_noalloc"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -319,6 +324,16 @@ def adamw_step_clipped(h, tensors, hp, max_norm, workspace, norm_out=None, strea
                                      workspace.numel() * workspace.element_size(),
                                      _stream_ptr(stream)),
            "adamw_step_clipped")
+
+
+def adamw_step_clipped_noalloc(h, tensors, hp, max_norm, norm_out=None, stream=None):
+    """adamw_step_clipped without a workspace: the library's fixed per-device
+    scratch holds the partial sums (at most 2^18 chunks of 4096 elements)."""
+    arr = (AdamwTensor * len(tensors))(*tensors)
+    _check(load().adamw_step_clipped_noalloc(
+        h, arr, len(tensors), ctypes.byref(hp), float(max_norm),
+        ctypes.c_void_p(norm_out.data_ptr() if norm_out is not None else 0), _stream_ptr(stream)),
+        "adamw_step_clipped_noalloc")
 
 
 def muon_test_gram_bf16(h, X, A, m, n, ldx, lda, s2=1.0, stream=None):

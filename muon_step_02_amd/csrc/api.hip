@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <numeric>
 #include <vector>
@@ -36,12 +37,47 @@ struct TimedLaunch {
 
 struct muon_context {
     int device = 0;
+    float* scratch = nullptr;  // this device's copy of `scratch` (below), device address
     int cus_per_xcd = 32;  // compute units per XCD (tile rounds)
     std::vector<char> table;  // host image of the descriptor table (reused)
     bool profiling = false;
     std::vector<TimedLaunch> timed;     // recorded since the last collect
     std::vector<hipEvent_t> event_pool;  // timing events ready for reuse
 };
+
+// Device scratch of the allocation-free entry point adamw_step_clipped_noalloc:
+// the per-chunk partial sums of squares (one per kAdamwChunk elements) and,
+// 256 bytes after the last of them, the clip scale.  Each device holds its
+// own copy for the life of the process.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device (resolve_scratch), never
+// the name itself.
+constexpr int kScratchBlocks = 1 << 18;              // 2^30 elements of AdamW tensors
+constexpr int kScratchFloats = kScratchBlocks + 64;  // + the scale, on its own 256 bytes
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<float*> g_scratch_addr;  // by device ordinal; null until resolved
+
+// Device address of `scratch` on `device`, which must be the current device.
+// Resolved once per device and kept.
+hipError_t resolve_scratch(int device, float** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if ((int)g_scratch_addr.size() <= device) g_scratch_addr.resize(device + 1, nullptr);
+    if (!g_scratch_addr[device]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[device] = static_cast<float*>(p);
+    }
+    *out = g_scratch_addr[device];
+    return hipSuccess;
+}
+
+}  // namespace
 
 namespace {
 
@@ -107,6 +143,7 @@ const char* muon_status_str(muon_status s) {
         case MUON_ERR_OVERLAP: return "param/grad/momentum/update ranges overlap";
         case MUON_ERR_HIP: return "HIP runtime error";
         case MUON_ERR_UNALIGNED: return "pointer not aligned to its element size";
+        case MUON_ERR_SCRATCH: return "problem larger than the fixed device scratch of the allocation-free entry point";
     }
     return "unknown status";
 }
@@ -125,6 +162,10 @@ muon_status muon_init(int device, muon_handle* out) {
     if (!h) return MUON_ERR_HIP;
     h->device = device;
     h->cus_per_xcd = prop.multiProcessorCount >= 8 ? prop.multiProcessorCount / 8 : 1;
+    if (resolve_scratch(device, &h->scratch) != hipSuccess) {
+        delete h;
+        return MUON_ERR_HIP;
+    }
     *out = h;
     return MUON_OK;
 }
@@ -341,23 +382,18 @@ muon_status adamw_workspace_size(muon_handle h, const adamw_tensor* ts, int n, s
     return MUON_OK;
 }
 
-muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
-                               const adamw_hparams* hp, float max_norm, float* norm_out,
-                               void* workspace, size_t workspace_bytes, void* stream) {
-    if (!h) return MUON_ERR_INVALID_ARG;
-    muon_status st = check_adamw(ts, n, hp);
-    if (st != MUON_OK) return st;
-    if (!finite(max_norm) || max_norm <= 0.f) return MUON_ERR_INVALID_ARG;
-    if (norm_out && reinterpret_cast<uintptr_t>(norm_out) % 4) return MUON_ERR_UNALIGNED;
-    const int64_t nblocks = adamw_total_blocks(ts, n);
-    const size_t need = align_up((size_t)nblocks * 4, 256) + 256;
-    const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
-    if (!workspace || ws % 256 || workspace_bytes < need) return MUON_ERR_WORKSPACE;
-    if (nblocks > INT32_MAX) return MUON_ERR_INVALID_ARG;
-    DeviceGuard g(h->device);
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float* partials = reinterpret_cast<float*>(workspace);
-    float* scale = reinterpret_cast<float*>(ws + align_up((size_t)nblocks * 4, 256));
+}  // extern "C"
+
+namespace {
+
+// Clipped AdamW with the partial sums at `partials` (nblocks floats) and the
+// scale at `scale`, both device memory; arguments already validated.  Every
+// partial is written by the sum-of-squares launch before the finalize reads
+// it, and the scale by the finalize before AdamW reads it: nothing needs to
+// start at zero.
+hipError_t clipped_launches(muon_context* h, const adamw_tensor* ts, int n, const adamw_hparams* hp,
+                            float max_norm, float* norm_out, float* partials, float* scale,
+                            int64_t nblocks, hipStream_t s) {
     hipError_t e = hipSuccess;
     if (nblocks > 0) {
         e = for_each_adamw_group(ts, n, [&](const AdamwGroup& grp, int blocks, int first) {
@@ -369,7 +405,54 @@ muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
             return launch_clip_finalize(partials, (int)nblocks, max_norm, scale, norm_out, s);
         });
     if (e == hipSuccess) e = adamw_launch_all(h, ts, n, hp, scale, s);
-    return hip_status(e);
+    return e;
+}
+
+muon_status check_clipped(muon_handle h, const adamw_tensor* ts, int n, const adamw_hparams* hp,
+                          float max_norm, float* norm_out) {
+    if (!h) return MUON_ERR_INVALID_ARG;
+    muon_status st = check_adamw(ts, n, hp);
+    if (st != MUON_OK) return st;
+    if (!finite(max_norm) || max_norm <= 0.f) return MUON_ERR_INVALID_ARG;
+    if (norm_out && reinterpret_cast<uintptr_t>(norm_out) % 4) return MUON_ERR_UNALIGNED;
+    if (adamw_total_blocks(ts, n) > INT32_MAX) return MUON_ERR_INVALID_ARG;
+    return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status adamw_step_clipped(muon_handle h, const adamw_tensor* ts, int n,
+                               const adamw_hparams* hp, float max_norm, float* norm_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    muon_status st = check_clipped(h, ts, n, hp, max_norm, norm_out);
+    if (st != MUON_OK) return st;
+    const int64_t nblocks = adamw_total_blocks(ts, n);
+    const size_t need = align_up((size_t)nblocks * 4, 256) + 256;
+    const uintptr_t ws = reinterpret_cast<uintptr_t>(workspace);
+    if (!workspace || ws % 256 || workspace_bytes < need) return MUON_ERR_WORKSPACE;
+    DeviceGuard g(h->device);
+    float* partials = reinterpret_cast<float*>(workspace);
+    float* scale = reinterpret_cast<float*>(ws + align_up((size_t)nblocks * 4, 256));
+    return hip_status(clipped_launches(h, ts, n, hp, max_norm, norm_out, partials, scale, nblocks,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+muon_status adamw_step_clipped_noalloc(muon_handle h, const adamw_tensor* ts, int n,
+                                       const adamw_hparams* hp, float max_norm, float* norm_out,
+                                       void* stream) {
+    muon_status st = check_clipped(h, ts, n, hp, max_norm, norm_out);
+    if (st != MUON_OK) return st;
+    const int64_t nblocks = adamw_total_blocks(ts, n);
+    if (nblocks > kScratchBlocks) return MUON_ERR_SCRATCH;
+    if (!h->scratch) return MUON_ERR_HIP;
+    DeviceGuard g(h->device);
+    // the device address resolved at init, never the host-side name
+    float* partials = h->scratch;
+    float* scale = h->scratch + kScratchBlocks;
+    return hip_status(clipped_launches(h, ts, n, hp, max_norm, norm_out, partials, scale, nblocks,
+                                       reinterpret_cast<hipStream_t>(stream)));
 }
 
 muon_status muon_profile_enable(muon_handle h, int enable) {
