@@ -157,11 +157,16 @@ def main():
     mu.muon_profile_enable(h, True)
     mu.muon_profile_collect(h)
     torch.cuda.synchronize()
+    # per-step events on the stream the steps run on (for the median)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for k in range(args.steps):
         step()
+        marks[k + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
     phases = mu.muon_profile_collect(h)
     mu.muon_profile_enable(h, False)
     ms_per_step = elapsed * 1e3 / args.steps
@@ -180,13 +185,17 @@ def main():
         per_launch_flops["update"] += 2 * m * m * n
         el += r * c
     peak_mm = PEAK_F32_TFLOPS if hpd["ns_dtype"] == "fp32" else PEAK_BF16_TFLOPS
+    # Per phase and Newton-Schulz iteration: every launch of the phase (one
+    # per size class in use, plus the reduce launch of a K-split Gram).
+    iters = args.steps * hpd["steps"]
     gemm = {}
     for ph in ("gram", "poly", "update"):
         ms, cnt = phases[ph]
-        avg = ms / max(cnt, 1)
-        tf = per_launch_flops[ph] / (avg * 1e-3) / 1e12 if avg > 0 else 0.0
-        gemm[ph] = {"avg_ms": round(avg, 4), "launches": cnt, "tflops": round(tf, 1),
-                    "frac": round(tf / peak_mm, 4)}
+        per_iter = ms / max(iters, 1)
+        tf = per_launch_flops[ph] / (per_iter * 1e-3) / 1e12 if per_iter > 0 else 0.0
+        gemm[ph] = {"avg_ms": round(per_iter, 4), "launches": cnt,
+                    "launches_per_iteration": round(cnt / max(iters, 1), 3),
+                    "tflops": round(tf, 1), "frac": round(tf / peak_mm, 4)}
     dom = max(("gram", "poly", "update"), key=lambda p: phases[p][0])
     # memory-bound kernels.  Algorithmic bytes per element: momentum reads G
     # and M, writes M and the Newton-Schulz input (G 4|2 + 4 + 4 + 2|4);
@@ -199,12 +208,14 @@ def main():
                 "apply": ((4 + ns_b + 4) * el, (4 + ns_b + 4) * el)}
     hbm = {}
     for ph, (b, b_act) in ew_bytes.items():
+        # per step: every launch of the phase (one per elementwise tile kind in use)
         ms, cnt = phases[ph]
-        avg = ms / max(cnt, 1)
+        avg = ms / max(args.steps, 1)
         gbs = b / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
         gbs_act = b_act / (avg * 1e-3) / 1e9 if avg > 0 else 0.0
-        hbm[ph] = {"avg_ms": round(avg, 4), "gb_s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
-                   "bytes_per_launch": b, "actual_gb_s": round(gbs_act, 1),
+        hbm[ph] = {"avg_ms": round(avg, 4), "launches_per_step": round(cnt / max(args.steps, 1), 3),
+                   "gb_s": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                   "bytes_per_step": b, "actual_gb_s": round(gbs_act, 1),
                    "actual_frac": round(gbs_act / PEAK_HBM_GBS, 4)}
     if ats:
         ad_el = sum(int(np.prod(wl.tensors[i].shape)) for i in wl.adamw)
@@ -219,7 +230,8 @@ def main():
     roofline = {"bound": "mfma", "kernel": "ns_update (X <- B X, B = aI + bA + cAA)" if dom == "update" else dom,
                 "achieved": gemm[dom]["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
                 "frac": gemm[dom]["frac"], "traffic": traffic,
-                "per_launch_flops": per_launch_flops[dom], "avg_launch_ms": dom_avg_ms}
+                "per_launch_flops": per_launch_flops[dom], "avg_launch_ms": dom_avg_ms,
+                "launches_per_iteration": gemm[dom]["launches_per_iteration"]}
 
     out = {
         "metric": "Muon step TFLOP/s (algorithmic, bf16 Newton-Schulz) and matrices/s",
@@ -229,6 +241,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

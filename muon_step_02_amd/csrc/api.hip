@@ -8,7 +8,7 @@
 //   momentum: one launch per elementwise tile kind in use (at most 3);
 //   norm finalize: one launch;
 //   ns_steps x {gram, poly, update}: one grouped launch per size class in use
-//     (at most 3) and phase;
+//     (at most 3) and phase, plus a reduce launch after a K-split Gram;
 //   apply: one launch per elementwise tile kind in use.
 #include <math.h>
 #include <string.h>
@@ -224,6 +224,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
     Prefix pc[kNumClasses];
     for (int c = 0; c < kNumClasses; ++c) {
         pc[c].gram = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pgram);
+        pc[c].tri = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_ptri);
         pc[c].upd = reinterpret_cast<const int32_t*>(ws + P.cls[c].off_pupd);
     }
 
@@ -243,15 +244,20 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             const MatDesc* dc = dd + C.first;
             e = timed(h, 2, s, [&] {
                 return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, s)
-                                 : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall, s);
+                                 : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall,
+                                                    C.gram_split, s);
             });
+            if (e == hipSuccess && C.gram_split)
+                e = timed(h, 2, s, [&] {
+                    return launch_gram_reduce_bf16(dc, C.count, pc[k], C.total_tri, it, k == kSmall, s);
+                });
         }
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
             e = timed(h, 3, s, [&] {
-                return k == kF32 ? launch_poly_f32(dc, C.count, pc[k], C.total_gram, b, c, s)
+                return k == kF32 ? launch_poly_f32(dc, C.count, pc[k], C.total_tri, b, c, s)
                                  : launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, a, b, c, k == kSmall, s);
             });
         }

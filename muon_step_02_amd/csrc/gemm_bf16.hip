@@ -75,6 +75,7 @@ struct Cfg {
     static constexpr int RPI = 64 / CH;        // rows per 1 KB slab copy
     static constexpr int STAGE = (BM + BN) * BK;  // bf16 elements per LDS stage
     static constexpr int LPS = ((BM + BN) / RPI) / NW;  // slab copies per stage per wave
+    static constexpr int LPS1 = (BM / RPI) / NW;        // ... when both operands are one slab
     // a stage is one LDS array (P slab, then Q slab) or, when each slab fills
     // an array by itself, two (P, Q)
     static constexpr int SPLIT = STAGE > kLdsArr ? 1 : 0;
@@ -232,6 +233,8 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 struct Epi {
     // output (row-major, ld) and, when `outT` is set, its transpose
     uint16_t* out;
+    // K-split Gram: the raw fp32 tile (row-major, ld BN) instead of `out`
+    float* outF;
     int64_t ld_out;
     uint16_t* outT;
     int64_t ld_outT;
@@ -246,12 +249,15 @@ struct Epi {
 };
 
 // Copy the operand slabs of k-range [k0, k0 + BK) into one LDS stage: the
-// BM x BK slab of P, then Q's (BN x BK, or BK x BN k-major).
-template <class C, bool QKN>
+// BM x BK slab of P, then Q's (BN x BK, or BK x BN k-major).  SAME: Q is the
+// same rows of the same matrix as P (a diagonal tile of a symmetric product),
+// whose fragments are then read from P's slab.
+template <class C, bool QKN, bool SAME = false>
 __device__ __forceinline__ void load_stage(const uint16_t* __restrict__ P0, int64_t ldp,
                                            const uint16_t* __restrict__ Q0, int64_t ldq,
                                            int64_t k0, const Stages& st, int i, int wave, int lane) {
     load_slab<C, C::BM>(P0 + k0, ldp, stage_p<C>(st, i), wave, lane);
+    if (SAME) return;
     if (QKN)
         load_slab_kn<C>(Q0 + k0 * ldq, ldq, stage_q<C>(st, i), wave, lane);
     else
@@ -265,11 +271,11 @@ struct Frags {
     bf16x8 a[C::FM], b[C::FN];
 };
 
-template <class C, bool QKN>
+template <class C, bool QKN, bool SAME = false>
 __device__ __forceinline__ void read_frags(const Stages& st, int i, int kk, int wm, int wn,
                                            int frow, int khalf, int lane, Frags<C>& f) {
     const uint16_t* sp = stage_p<C>(st, i);
-    const uint16_t* sq = stage_q<C>(st, i);
+    const uint16_t* sq = SAME ? sp : stage_q<C>(st, i);
     const int lch = 2 * kk + khalf;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
@@ -328,7 +334,7 @@ __device__ __forceinline__ void load_e_band(const Epi& ep, int64_t row0, int64_t
 // dimension ldp) and BN columns of Q' (K a multiple of BK), then the
 // epilogue.  Q' is read as Q'[k][j] = Q0[j * ldq + k] (NT) or, with QKN, as
 // Q0[k * ldq + j] (k-major).
-template <class C, bool HAS_E, bool QKN = false>
+template <class C, bool HAS_E, bool QKN = false, bool F32OUT = false, bool SAME = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64_t ldp,
                                           const uint16_t* __restrict__ Q0, int64_t ldq, int K,
                                           int64_t row0, int64_t col0, const Epi& ep,
@@ -359,13 +365,14 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
     for (int u = 0; u < C::NS; ++u) {
         if (u < KT) {
-            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, st, u, wave, lane);
+            load_stage<C, QKN, SAME>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, st, u, wave, lane);
         }
     }
-    if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * C::LPS>(); else wait_vmcnt<0>();
+    constexpr int LPS = SAME ? C::LPS1 : C::LPS;
+    if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * LPS>(); else wait_vmcnt<0>();
     __syncthreads();
     Frags<C> f[2];
-    read_frags<C, QKN>(st, 0, 0, wm, wn, frow, khalf, lane, f[0]);
+    read_frags<C, QKN, SAME>(st, 0, 0, wm, wn, frow, khalf, lane, f[0]);
 
     for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
 #pragma unroll
@@ -375,7 +382,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     if (kk + 1 < KS) {
-                        read_frags<C, QKN>(st, u, kk + 1, wm, wn, frow, khalf, lane,
+                        read_frags<C, QKN, SAME>(st, u, kk + 1, wm, wn, frow, khalf, lane,
                                            f[(kk + 1) & 1]);
                     } else {
                         // slab kt + 1 has landed once only the copies of the
@@ -383,13 +390,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                         // The last slab takes the same path (its reads of
                         // the next stage are unused) so every slab has one
                         // straight-line sequence of LDS waits.
-                        if (kt + C::NS - 1 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
+                        if (kt + C::NS - 1 < KT) wait_vmcnt<(C::NS - 2) * LPS>(); else wait_vmcnt<0>();
                         __syncthreads();
                         if (kt + C::NS < KT) {
-                            load_stage<C, QKN>(P0, ldp, Q0, ldq, (int64_t)(kt + C::NS) * C::BK,
+                            load_stage<C, QKN, SAME>(P0, ldp, Q0, ldq, (int64_t)(kt + C::NS) * C::BK,
                                                st, u, wave, lane);
                         }
-                        read_frags<C, QKN>(st, (u + 1) % C::NS, 0, wm, wn, frow, khalf, lane, f[0]);
+                        read_frags<C, QKN, SAME>(st, (u + 1) % C::NS, 0, wm, wn, frow, khalf, lane, f[0]);
                     }
                     mfma_frags<C>(acc, f[kk & 1]);
                     // two reads with each of the first MFMAs: the reads go out early
@@ -459,6 +466,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] += (dc == e) ? ep.diag : 0.f;
             }
+            if constexpr (F32OUT) {
+                // a partial tile of a K-split Gram: fp32, tile-local, no mirror
+                float* o = ep.outF + (int64_t)(band * C::RB + rr) * C::BN + c8;
+                gst(reinterpret_cast<float4*>(o), make_float4(v[0], v[1], v[2], v[3]));
+                gst(reinterpret_cast<float4*>(o + 4), make_float4(v[4], v[5], v[6], v[7]));
+                continue;
+            }
             uint4 o;
             o.x = pack2(v[0], v[1]);
             o.y = pack2(v[2], v[3]);
@@ -470,7 +484,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                 *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
             }
         }
-        if (ep.outT) {
+        if (!F32OUT && ep.outT) {
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
@@ -570,6 +584,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
     const bool on_diag = ti == tj && (q < 0 || (q >> 1) == (q & 1));
     const int64_t mp = d.mp, np = d.np;
     Epi ep;
+    ep.outF = nullptr;
     ep.out = reinterpret_cast<uint16_t*>(PHASE == GRAM ? d.a : d.b);
     ep.ld_out = mp;
     ep.outT = on_diag ? nullptr : ep.out;
@@ -596,15 +611,138 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
         ep.post = 1.f;
         ep.diag = on_diag ? ca : 0.f;
     }
+    // a tile (or quarter) on the diagonal multiplies the same rows by
+    // themselves: one slab copy serves both operands
     if (q < 0) {
         const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-        gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+        if (on_diag)
+            gemm_tile<C, PHASE == POLY, false, false, true>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld,
+                                                             r0, c0, ep, st);
+        else
+            gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
     } else if constexpr (C::BM == 256) {
         using Q = QuarterCfg<C>;
         const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
         const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
-        gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
+        if (on_diag)
+            gemm_tile<Q, PHASE == POLY, false, false, true>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld,
+                                                             r0, c0, ep, st);
+        else
+            gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, (int)ld, r0, c0, ep, st);
     }
+}
+
+// K-split Gram (launches with fewer tiles than compute units): task t of a
+// matrix is part t / T of triangle tile t % T (T tiles), i.e. the product
+// over K slabs [part * slabs / S, (part + 1) * slabs / S) of S; its raw fp32
+// tile goes to gram_part[t].  ns_gram_reduce_kernel then forms A.
+template <class C>
+__global__ __launch_bounds__(C::NT) void ns_gram_split_kernel(const MatDesc* __restrict__ descs, int n,
+                                                              const int32_t* __restrict__ prefix,
+                                                              XcdSplit xs, int it) {
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[C::NARR > 1 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds2[C::NARR > 2 ? kLdsArr : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds3[C::NARR > 3 ? kLdsArr : 8];
+    const Stages st{{lds0, lds1, lds2, lds3}};
+    int task, q;
+    if (!xcd_task(xs, task, q)) return;  // no quarter tasks: the split launch fits one round
+    const int mi = find_matrix(prefix, n, task);
+    const MatDesc& d = descs[mi];
+    const int lt = task - prefix[mi];
+    const int64_t np = d.np;
+    const int tm = (int)(d.mp / C::BM);
+    const int T = tm * (tm + 1) / 2;
+    const int part = lt / T;
+    int ti, tj;
+    tri_index(lt - part * T, ti, tj);
+    const int S = d.gram_split;
+    const int slabs = (int)(np / C::BK);
+    const int64_t k0 = (int64_t)(part * slabs / S) * C::BK;
+    const int64_t k1 = (int64_t)((part + 1) * slabs / S) * C::BK;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+    Epi ep;
+    ep.outF = d.gram_part + (int64_t)lt * C::BM * C::BN;
+    ep.out = nullptr;
+    ep.ld_out = 0;
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
+    ep.coef_acc = 1.f;
+    ep.post = 1.f;
+    ep.diag = 0.f;
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    if (ti == tj)
+        gemm_tile<C, false, false, true, true>(src + r0 * np + k0, np, src + c0 * np + k0, np,
+                                               (int)(k1 - k0), 0, 0, ep, st);
+    else
+        gemm_tile<C, false, false, true>(src + r0 * np + k0, np, src + c0 * np + k0, np, (int)(k1 - k0),
+                                         0, 0, ep, st);
+}
+
+// Sum of the K-parts of a split Gram, in part order (so the result does not
+// depend on timing), scaled by s^2 on the first iteration, rounded to bf16
+// and stored into A at the tile and, off the diagonal, at its mirror.  One
+// workgroup per 64 x 64 chunk of a triangle tile; thread t: row t / 4,
+// columns 16 (t % 4) ... + 15 of the chunk.
+template <int BT>
+__global__ __launch_bounds__(256) void ns_gram_reduce_kernel(const MatDesc* __restrict__ descs, int n,
+                                                             const int32_t* __restrict__ prefix_tri,
+                                                             int it) {
+    constexpr int CH = BT / 64;
+    __shared__ float tr[64][65];
+    const int g = blockIdx.x;
+    const int tile = g / (CH * CH);
+    const int chunk = g - tile * (CH * CH);
+    const int mi = find_matrix(prefix_tri, n, tile);
+    const MatDesc& d = descs[mi];
+    const int lt = tile - prefix_tri[mi];
+    const int T = prefix_tri[mi + 1] - prefix_tri[mi];
+    int ti, tj;
+    tri_index(lt, ti, tj);
+    const int cr = chunk / CH, cc = chunk - cr * CH;
+    const int S = d.gram_split;
+    const int r = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = 0.f;
+    for (int p = 0; p < S; ++p) {
+        const float* src = d.gram_part + ((int64_t)(p * T + lt) * BT + cr * 64 + r) * BT + cc * 64 + c16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = gld(reinterpret_cast<const float4*>(src + 4 * q));
+            v[4 * q] += f.x;
+            v[4 * q + 1] += f.y;
+            v[4 * q + 2] += f.z;
+            v[4 * q + 3] += f.w;
+        }
+    }
+    const float s = it == 0 ? gld(d.inv_norm) : 1.f;
+    const float s2 = s * s;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] *= s2;
+    uint16_t* A = reinterpret_cast<uint16_t*>(d.a);
+    const int64_t lda = d.mp;
+    const int64_t row = (int64_t)ti * BT + cr * 64 + r, col = (int64_t)tj * BT + cc * 64 + c16;
+    uint4 o0, o1;
+    o0.x = pack2(v[0], v[1]); o0.y = pack2(v[2], v[3]); o0.z = pack2(v[4], v[5]); o0.w = pack2(v[6], v[7]);
+    o1.x = pack2(v[8], v[9]); o1.y = pack2(v[10], v[11]); o1.z = pack2(v[12], v[13]); o1.w = pack2(v[14], v[15]);
+    gst(reinterpret_cast<uint4*>(A + row * lda + col), o0);
+    gst(reinterpret_cast<uint4*>(A + row * lda + col + 8), o1);
+    if (ti == tj) return;  // a diagonal tile is computed whole: no mirror
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tr[r][c16 + e] = v[e];
+    __syncthreads();
+    float w[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[e] = tr[c16 + e][r];
+    const int64_t trow = (int64_t)tj * BT + cc * 64 + r, tcol = (int64_t)ti * BT + cr * 64 + c16;
+    o0.x = pack2(w[0], w[1]); o0.y = pack2(w[2], w[3]); o0.z = pack2(w[4], w[5]); o0.w = pack2(w[6], w[7]);
+    o1.x = pack2(w[8], w[9]); o1.y = pack2(w[10], w[11]); o1.z = pack2(w[12], w[13]); o1.w = pack2(w[14], w[15]);
+    gst(reinterpret_cast<uint4*>(A + trow * lda + tcol), o0);
+    gst(reinterpret_cast<uint4*>(A + trow * lda + tcol + 8), o1);
 }
 
 template <class C>
@@ -628,6 +766,7 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
     const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
     Epi ep;
+    ep.outF = nullptr;
     ep.out = reinterpret_cast<uint16_t*>(d.x[(it + 1) & 1]);
     ep.ld_out = np;
     ep.outT = nullptr;
@@ -668,6 +807,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
     if (q >= 0 && ti == tj && (q >> 1) < (q & 1)) return;
     const bool on_diag = ti == tj && (q < 0 || (q >> 1) == (q & 1));
     Epi ep;
+    ep.outF = nullptr;
     ep.out = out;
     ep.ld_out = ld_out;
     ep.outT = on_diag ? nullptr : out;
@@ -681,12 +821,20 @@ __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restric
     }
     if (q < 0) {
         const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
-        gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+        if (on_diag)
+            gemm_tile<C, PHASE == POLY, false, false, true>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0,
+                                                             ep, st);
+        else
+            gemm_tile<C, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
     } else {
         using Q = QuarterCfg<C>;
         const int64_t r0 = (int64_t)ti * C::BM + (q >> 1) * Q::BM;
         const int64_t c0 = (int64_t)tj * C::BN + (q & 1) * Q::BN;
-        gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
+        if (on_diag)
+            gemm_tile<Q, PHASE == POLY, false, false, true>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0,
+                                                             ep, st);
+        else
+            gemm_tile<Q, PHASE == POLY>(src + r0 * ld, ld, src + c0 * ld, ld, K, r0, c0, ep, st);
     }
 }
 
@@ -706,6 +854,7 @@ __global__ __launch_bounds__(C::NT) void ns_update_single(const uint16_t* __rest
     int ti, tj;
     grouped_index(tile, m / C::BM, n / C::BN, ti, tj);
     Epi ep;
+    ep.outF = nullptr;
     ep.out = Xo; ep.ld_out = ldx; ep.outT = nullptr; ep.ld_outT = 0;
     ep.E = nullptr; ep.ld_e = 0; ep.coef_e = 0.f; ep.coef_acc = 1.f; ep.post = s; ep.diag = 0.f;
     if (q < 0) {
@@ -735,7 +884,14 @@ static_assert(SmallCfg::BM == kClassTile[kSmall] && SmallCfg::BN == kClassTile[k
               "128-class tiles");
 
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
-                            int small, hipStream_t st) {
+                            int small, int split, hipStream_t st) {
+    if (split) {
+        if (small)
+            ns_gram_split_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, it);
+        else
+            ns_gram_split_kernel<SymCfg><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, it);
+        return hipGetLastError();
+    }
     if (small)
         ns_sym_kernel<SmallCfg, GRAM><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, it, 0.f, 0.f, 0.f);
     else
@@ -743,12 +899,23 @@ hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& x
     return hipGetLastError();
 }
 
+hipError_t launch_gram_reduce_bf16(const MatDesc* d, int n, Prefix p, int tiles, int it, int small,
+                                   hipStream_t st) {
+    if (small)
+        ns_gram_reduce_kernel<SmallCfg::BM><<<tiles * (SmallCfg::BM / 64) * (SmallCfg::BM / 64), 256, 0, st>>>(
+            d, n, p.tri, it);
+    else
+        ns_gram_reduce_kernel<SymCfg::BM><<<tiles * (SymCfg::BM / 64) * (SymCfg::BM / 64), 256, 0, st>>>(
+            d, n, p.tri, it);
+    return hipGetLastError();
+}
+
 hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float a,
                             float b, float c, int small, hipStream_t st) {
     if (small)
-        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, a, b, c);
+        ns_sym_kernel<SmallCfg, POLY><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.tri, xs, 0, a, b, c);
     else
-        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.gram, xs, 0, a, b, c);
+        ns_sym_kernel<SymCfg, POLY><<<xcd_grid(xs), SymCfg::NT, 0, st>>>(d, n, p.tri, xs, 0, a, b, c);
     return hipGetLastError();
 }
 

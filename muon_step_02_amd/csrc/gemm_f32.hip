@@ -140,7 +140,7 @@ hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it,
 
 hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
                            hipStream_t st) {
-    ns_f32_kernel<POLY><<<total, 256, 0, st>>>(d, n, p.gram, 0, 0.f, b, c);
+    ns_f32_kernel<POLY><<<total, 256, 0, st>>>(d, n, p.tri, 0, 0.f, b, c);
     return hipGetLastError();
 }
 

@@ -24,6 +24,11 @@ constexpr int kTinyF32 = 32;
 constexpr int kClassPad[kNumClasses] = {256, 128, 64};
 constexpr int kClassTile[kNumClasses] = {256, 128, 64};  // square tiles, all three phases
 constexpr int kTileF32 = 64;
+// Split-K of tile-starved Gram launches: a part covers at least kMinSplitSlabs
+// 64-wide K slabs, and a tile has at most kMaxSplit parts.
+constexpr int kGemmBK = 64;
+constexpr int kMinSplitSlabs = 8;
+constexpr int kMaxSplit = 16;
 
 // Elementwise kernels (momentum, apply) work on tiles of the weight, one
 // kind per launch:
@@ -62,6 +67,7 @@ struct MatDesc {
     int32_t ew_tiles;      // elementwise tiles of this matrix (one norm partial each)
     int32_t vec4;        // 1: every row start of param/grad/mom is 16B aligned and cols % 4 == 0
     int32_t cls;         // SizeClass
+    int32_t gram_split;  // K-parts of each Gram tile (1: unsplit; see Prefix)
     float scale;         // shape multiplier * extra_scale
     // workspace buffers (bf16, or f32 elements for the kF32 class)
     void* x[2];   // canonical X, mp x np, ld np (ping-pong)
@@ -70,12 +76,21 @@ struct MatDesc {
     void* b;      // B = a I + b A + c A A, mp x mp
     float* partials;  // one sum of squares per elementwise tile
     float* inv_norm;  // s = 1/(||Y||_F + eps)
+    float* gram_part; // split Gram: fp32 partial tiles [part][tile][BM][BN] (task order)
 };
 
-// Grouped launches: workgroup -> (matrix, local tile) through prefix sums of
-// tiles per matrix (int32 entries, n+1 of them).
+// Grouped launches: workgroup -> (matrix, local task) through prefix sums of
+// tasks per matrix (int32 entries, n+1 of them).
+//
+// A Gram launch with too few tiles to fill the chip (less than one tile per
+// compute unit) is split along K: matrix k's Gram tiles are computed in
+// gram_split parts of its K range each, as fp32 partial tiles, and a reduce
+// launch sums the parts in a fixed order and writes A (scaled, rounded,
+// mirrored).  Its Gram launch then runs tiles * gram_split tasks (part-major:
+// task t is part t / tiles of tile t % tiles).
 struct Prefix {
-    const int32_t* gram;  // Gram and polynomial tiles
+    const int32_t* gram;  // Gram tasks (tiles, or tiles * gram_split when split)
+    const int32_t* tri;   // triangle tiles (polynomial; reduce of a split Gram)
     const int32_t* upd;   // update tiles
 };
 

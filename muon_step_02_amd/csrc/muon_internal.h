@@ -80,14 +80,19 @@ hipError_t launch_apply(const MatDesc* d, int n, const EwGroups& g, int final_pa
 // kSmall).  `it` is the iteration index (0-based): it selects the ping-pong
 // buffers and, for it == 0, folds the normalisation s = 1/(||Y||+eps) into
 // the epilogues.  Tiles are dealt to XCDs by `xs` (see XcdSplit).
+// split: the class's Gram launch is K-split (p.gram counts tasks); the reduce
+// launch (over p.tri's `tiles` triangle tiles) then forms A
 hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
-                            int small, hipStream_t st);
+                            int small, int split, hipStream_t st);
+hipError_t launch_gram_reduce_bf16(const MatDesc* d, int n, Prefix p, int tiles, int it, int small,
+                                   hipStream_t st);
 // poly writes B = a I + b A + c A A, so the update is the plain product B X
 hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float a,
                             float b, float c, int small, hipStream_t st);
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                               int small, hipStream_t st);
 
+// fp32 class (every tile of the symmetric products; p.gram == p.tri)
 hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
 hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
                            hipStream_t st);

@@ -157,6 +157,37 @@ XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus,
     return xs;
 }
 
+std::vector<int32_t> gram_splits(const std::vector<int32_t>& tiles,
+                                 const std::vector<int32_t>& slabs, int cus_total) {
+    const size_t n = tiles.size();
+    std::vector<int32_t> S(n, 1);
+    int64_t total = 0, work = 0, longest = 0;
+    for (size_t k = 0; k < n; ++k) {
+        total += tiles[k];
+        work += (int64_t)tiles[k] * slabs[k];
+        longest = std::max<int64_t>(longest, slabs[k]);
+    }
+    // Split only a launch whose tiles fill at most a quarter of the slots:
+    // with every compute unit busy a tile's K loop runs about twice as slowly
+    // per slab as in a launch that leaves most of the chip idle, and the
+    // reduce launch re-reads the partial tiles, so fewer than four parts per
+    // tile do not pay (measured on the d=1024 block: 70 tiles of up to 64
+    // slabs, split or not, both about 52 us).
+    if (total == 0 || 4 * total > cus_total) return S;
+    // parts of at least `len` slabs each
+    auto parts = [&](size_t k, int64_t len) {
+        return (int32_t)std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, slabs[k] / len));
+    };
+    int64_t len = std::max<int64_t>(kMinSplitSlabs, (work + cus_total - 1) / cus_total);
+    for (; len < longest; ++len) {
+        int64_t tasks = 0;
+        for (size_t k = 0; k < n; ++k) tasks += (int64_t)tiles[k] * parts(k, len);
+        if (tasks <= cus_total) break;
+    }
+    for (size_t k = 0; k < n; ++k) S[k] = parts(k, len);
+    return S;
+}
+
 // Workspace plan for one call.  Matrices are split into the size classes of
 // layout.h, each with its own GEMM tile and padding and its own prefix arrays
 // of Gram/polynomial and update tiles; the descriptor table holds kLarge
@@ -202,6 +233,7 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         C.count = count[c];
         first += count[c];
         C.pgram.assign(C.count + 1, 0);
+        C.ptri.assign(C.count + 1, 0);
         C.pupd.assign(C.count + 1, 0);
     }
     int64_t tew = 0, tek[kNumEwKinds] = {0, 0, 0};
@@ -255,6 +287,7 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
                  aligned_rows(m.grad, m.ld_grad, elem_bytes(m.grad_dtype)) &&
                  aligned_rows(m.momentum, m.ld_mom, 4);
         d.scale = (float)(shape_multiplier(hp->scale_mode, m.rows, m.cols) * (double)hp->extra_scale);
+        d.gram_split = 1;
         const int64_t Ts = d.mp / tile;
         // the bf16 kernels compute the symmetric products on the lower
         // triangle of tiles; the fp32 ones compute every tile
@@ -269,28 +302,50 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         P.pew[k + 1] = (int32_t)tew;
         for (int kk = 0; kk < kNumEwKinds; ++kk) P.pek[kk][k + 1] = (int32_t)tek[kk];
         const int kc = k - P.cls[c].first;
-        P.cls[c].pgram[kc + 1] = (int32_t)tgram[c];
+        P.cls[c].ptri[kc + 1] = (int32_t)tgram[c];
         P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
     }
     for (int kind = 0; kind < kNumEwKinds; ++kind) P.total_ek[kind] = (int)tek[kind];
     for (int c = 0; c < kNumClasses; ++c) {
         ClassPlan& C = P.cls[c];
-        C.total_gram = (int)tgram[c];
+        C.total_tri = (int)tgram[c];
         C.total_upd = (int)tupd[c];
+        std::vector<int32_t> tg(C.count), tu(C.count), slabs(C.count);
+        for (int k = 0; k < C.count; ++k) {
+            tg[k] = C.ptri[k + 1] - C.ptri[k];
+            tu[k] = C.pupd[k + 1] - C.pupd[k];
+            slabs[k] = P.d[C.first + k].np / kGemmBK;
+        }
+        // Gram tasks: its tiles, or tiles * parts when the launch is K-split
+        std::vector<int32_t> S(C.count, 1);
+        // compute slots: two 128-tile workgroups fit one compute unit's LDS
+        const int slots = 8 * cus * (c == kSmall ? 2 : 1);
+        if (c != kF32 && C.count > 0) S = gram_splits(tg, slabs, slots);
+        int64_t tasks = 0;
+        for (int k = 0; k < C.count; ++k) {
+            P.d[C.first + k].gram_split = S[k];
+            C.gram_split = C.gram_split || S[k] > 1;
+        }
+        for (int k = 0; k < C.count; ++k) {
+            tasks += (int64_t)tg[k] * (C.gram_split ? S[k] : 1);
+            if (tasks > INT32_MAX / 2) return MUON_ERR_INVALID_ARG;
+            C.pgram[k + 1] = (int32_t)tasks;
+        }
+        C.total_gram = (int)tasks;
         if (c == kF32 || C.count == 0) continue;
-        // tile work = k-steps: the Gram runs over n', the polynomial and the
-        // update over m'
-        std::vector<int32_t> tg(C.count), tu(C.count);
+        // tile work = k-steps: the Gram runs over n' (a part of it when
+        // split), the polynomial and the update over m'
+        std::vector<int32_t> tk(C.count);
         std::vector<int64_t> wn(C.count), wm(C.count);
         for (int k = 0; k < C.count; ++k) {
-            tg[k] = C.pgram[k + 1] - C.pgram[k];
-            tu[k] = C.pupd[k + 1] - C.pupd[k];
-            wn[k] = P.d[C.first + k].np;
+            tk[k] = C.pgram[k + 1] - C.pgram[k];
+            wn[k] = C.gram_split ? (slabs[k] + S[k] - 1) / S[k] : P.d[C.first + k].np;
             wm[k] = P.d[C.first + k].mp;
         }
-        // quarter tiles for the short last round: 256-tile class only
+        // quarter tiles for the short last round: 256-tile class only, and not
+        // in a K-split Gram (its tasks fit one round)
         const int quarters = c == kLarge ? 1 : 0;
-        C.xs_gram = xcd_split(tg.data(), wn.data(), C.count, cus, quarters);
+        C.xs_gram = xcd_split(tk.data(), wn.data(), C.count, cus, C.gram_split ? 0 : quarters);
         C.xs_poly = xcd_split(tg.data(), wm.data(), C.count, cus, quarters);
         C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters);
     }
@@ -302,6 +357,8 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
     }
     for (int c = 0; c < kNumClasses; ++c) {
         P.cls[c].off_pgram = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+        P.cls[c].off_ptri = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
         P.cls[c].off_pupd = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
@@ -331,6 +388,15 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         off = align_up(off + ab, 256);
         d.partials = reinterpret_cast<float*>(ws + P.off_partials) + P.pew[k];
         d.inv_norm = reinterpret_cast<float*>(ws + P.off_invnorm) + k;
+        d.gram_part = nullptr;
+        const ClassPlan& C = P.cls[d.cls];
+        if (C.gram_split) {
+            const int kc = k - C.first;
+            const size_t tile = (size_t)kClassTile[d.cls];
+            const size_t tasks = (size_t)(C.pgram[kc + 1] - C.pgram[kc]);
+            d.gram_part = reinterpret_cast<float*>(ws + off);
+            off = align_up(off + tasks * tile * tile * 4, 256);
+        }
     }
     P.total = off;
     return MUON_OK;
@@ -349,7 +415,9 @@ void table_image(const Plan& P, std::vector<char>& out) {
     for (const ClassPlan& c : P.cls) {
         PLAN_CHECK(c.off_pgram + (size_t)(c.count + 1) * 4 <= P.table_bytes);
         PLAN_CHECK(c.off_pupd + (size_t)(c.count + 1) * 4 <= P.table_bytes);
+        PLAN_CHECK(c.off_ptri + (size_t)(c.count + 1) * 4 <= P.table_bytes);
         memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
+        memcpy(hb + c.off_ptri, c.ptri.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
     }
 }
@@ -360,7 +428,7 @@ std::vector<int> split_matrices(const Plan& P) {
         const ClassPlan& C = P.cls[c];
         if (C.count == 0) continue;
         const XcdSplit* splits[3] = {&C.xs_gram, &C.xs_poly, &C.xs_upd};
-        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.pgram, &C.pupd};
+        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.ptri, &C.pupd};
         for (int s = 0; s < 3; ++s) {
             const XcdSplit& xs = *splits[s];
             const std::vector<int32_t>& pre = *prefixes[s];

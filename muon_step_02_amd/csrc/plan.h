@@ -17,9 +17,10 @@ namespace muon {
 // Tiles and launch ranges of one size class.
 struct ClassPlan {
     int first = 0, count = 0;           // descriptor range [first, first + count)
-    std::vector<int32_t> pgram, pupd;   // count + 1 entries each
-    size_t off_pgram = 0, off_pupd = 0; // their offsets in the workspace
-    int total_gram = 0, total_upd = 0;
+    std::vector<int32_t> pgram, ptri, pupd;      // count + 1 entries each (see Prefix)
+    size_t off_pgram = 0, off_ptri = 0, off_pupd = 0;  // their offsets in the workspace
+    int total_gram = 0, total_tri = 0, total_upd = 0;
+    bool gram_split = false;            // the Gram launch runs K-split (bf16 classes)
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };
 
@@ -42,6 +43,15 @@ struct Plan {
 // MUON_OK leaves P unspecified.
 muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
                       uintptr_t ws, int cus, Plan& P);
+
+// K-parts per matrix for a Gram launch over `tiles[k]` tiles of `slabs[k]`
+// 64-wide K slabs each, with `cus_total` workgroup slots: all 1 unless the
+// tiles fill at most a quarter of the slots; then, for the shortest part
+// length L (at least kMinSplitSlabs, and at least the total work over
+// cus_total) at which the tasks still fit one round, floor(slabs / L) parts
+// (between 1 and kMaxSplit), so every part holds at least L slabs.
+std::vector<int32_t> gram_splits(const std::vector<int32_t>& tiles,
+                                 const std::vector<int32_t>& slabs, int cus_total);
 
 // Host image of the workspace's first P.table_bytes bytes: the descriptors
 // and every prefix array.

@@ -280,8 +280,50 @@ def headline(n=8, dim=4096):
                     muon, [], steps=1, muon_hp=dict(MUON_DEFAULT))
 
 
+def headline_fp32(n=2, dim=4096):
+    """The headline matrices with the fp32 iteration (its throughput at a
+    size where it is not launch-bound)."""
+    w = headline(n=n, dim=dim)
+    w.muon_hp = dict(MUON_DEFAULT, ns_dtype="fp32")
+    w.name = "%dx %dx%d fp32 weights, fp32 Newton-Schulz" % (n, dim, dim)
+    return w
+
+
+def perhead(n_heads=64, head_dim=128, d_model=7168):
+    """Per-head Muon: the query projection of a d_model=7168, 64-head
+    attention layer (8192 x 7168, Kimi K2's shape) orthogonalised one head at
+    a time, i.e. 64 row blocks of 128 x 7168 of one fused tensor.  Gradient:
+    rank-32 spikes 10^(-i/8) + noise over the fused tensor (as config 3)."""
+    rec = GradRecipe("lowrank", rank=32, decay=0.125, noise_std=1e-3)
+    t = [_muon_tensor("wq", n_heads * head_dim, d_model, rec)]
+    muon = [MuonView(0, h * head_dim, head_dim) for h in range(n_heads)]
+    return Workload("per-head Muon: %d heads x %dx%d (row blocks of a %dx%d query projection)"
+                    % (n_heads, head_dim, d_model, n_heads * head_dim, d_model),
+                    200, t, muon, [], steps=1, muon_hp=dict(MUON_DEFAULT))
+
+
+def perhead_mixed(n_heads=32, head_dim=128, d_model=4096):
+    """Per-head and whole matrices in one call: the query and key projections
+    of a d_model=4096, 32-head layer split per head (64 blocks of 128 x 4096)
+    beside the unsplit value and output projections (4096 x 4096 each)."""
+    rec = GradRecipe("lowrank", rank=16, decay=0.25, noise_std=1e-3)
+    t, muon = [], []
+    for name in ("wq", "wk"):
+        idx = len(t)
+        t.append(_muon_tensor(name, n_heads * head_dim, d_model, rec))
+        muon += [MuonView(idx, h * head_dim, head_dim) for h in range(n_heads)]
+    for name in ("wv", "wo"):
+        muon.append(MuonView(len(t), 0, d_model))
+        t.append(_muon_tensor(name, d_model, d_model, rec))
+    return Workload("per-head Q/K (%d x %dx%d each) + whole V, O (%dx%d)"
+                    % (n_heads, head_dim, d_model, d_model, d_model),
+                    201, t, muon, [], steps=1, muon_hp=dict(MUON_DEFAULT))
+
+
 WORKLOADS = {"c0": config0, "c1": config1, "c2": config2, "c3": config3, "c4": config4,
              "headline": headline,
              # the same matrices, fewer of them: one 4096^2 matrix leaves most
              # of the chip idle (136 Gram tiles against 256 CUs)
-             "headline-1": lambda: headline(n=1), "headline-2": lambda: headline(n=2)}
+             "headline-1": lambda: headline(n=1), "headline-2": lambda: headline(n=2),
+             "headline-2-fp32": lambda: headline_fp32(n=2),
+             "perhead": perhead, "perhead-mixed": perhead_mixed}

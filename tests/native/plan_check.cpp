@@ -186,7 +186,31 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         g_run[d.cls] += d.cls == kF32 ? Ts * Ts : Ts * (Ts + 1) / 2;
         u_run[d.cls] += (d.mp / tile) * (d.np / tile);
         const int kc = k - C.first;
-        EXPECT(C.pgram[kc + 1] == g_run[d.cls] && C.pupd[kc + 1] == u_run[d.cls]);
+        EXPECT(C.ptri[kc + 1] == g_run[d.cls] && C.pupd[kc + 1] == u_run[d.cls]);
+        // Gram tasks: the triangle tiles, times the K-parts when the class splits
+        const int64_t tri = C.ptri[kc + 1] - C.ptri[kc];
+        EXPECT(d.gram_split >= 1 && d.gram_split <= kMaxSplit);
+        if (!C.gram_split) EXPECT(d.gram_split == 1 && C.pgram[kc + 1] == C.ptri[kc + 1]);
+        if (C.gram_split) {
+            EXPECT(d.cls != kF32);
+            EXPECT(C.pgram[kc + 1] - C.pgram[kc] == tri * d.gram_split);
+            // the kernel's part ranges cover the K slabs once, each part >= kMinSplitSlabs
+            const int slabs = d.np / kGemmBK, S = d.gram_split;
+            int covered = 0;
+            for (int part = 0; part < S; ++part) {
+                const int k0 = part * slabs / S, k1 = (part + 1) * slabs / S;
+                EXPECT(k0 == covered && k1 > k0);
+                if (S > 1) EXPECT(k1 - k0 >= kMinSplitSlabs);
+                covered = k1;
+            }
+            EXPECT(covered == slabs);
+            const size_t tt = (size_t)kClassTile[d.cls];
+            EXPECT(d.gram_part != nullptr);
+            iv.push_back({(uintptr_t)d.gram_part,
+                          (uintptr_t)d.gram_part + (size_t)(tri * d.gram_split) * tt * tt * 4, "part"});
+        } else {
+            EXPECT(d.gram_part == nullptr);
+        }
         // workspace buffers
         const size_t es = d.cls == kF32 ? 4 : 2;
         const size_t xb = (size_t)d.mp * d.np * es, ab = (size_t)d.mp * d.mp * es;
@@ -215,8 +239,16 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
     for (int kind = 0; kind < kNumEwKinds; ++kind)
         tv.push_back({P.off_pek[kind], P.off_pek[kind] + 4 * (size_t)(n + 1), "pek"});
     for (int c = 0; c < kNumClasses; ++c) {
-        EXPECT(P.cls[c].total_gram == g_run[c] && P.cls[c].total_upd == u_run[c]);
+        EXPECT(P.cls[c].total_tri == g_run[c] && P.cls[c].total_upd == u_run[c]);
+        EXPECT(P.cls[c].total_gram == P.cls[c].pgram[P.cls[c].count]);
+        // a split launch fits one round; a launch is split only when starved
+        if (P.cls[c].gram_split) {
+            const int slots = 8 * cus * (c == kSmall ? 2 : 1);
+            EXPECT(P.cls[c].total_gram <= slots);
+            EXPECT(4 * P.cls[c].total_tri <= slots);
+        }
         tv.push_back({P.cls[c].off_pgram, P.cls[c].off_pgram + 4 * (size_t)(P.cls[c].count + 1), "pg"});
+        tv.push_back({P.cls[c].off_ptri, P.cls[c].off_ptri + 4 * (size_t)(P.cls[c].count + 1), "pt"});
         tv.push_back({P.cls[c].off_pupd, P.cls[c].off_pupd + 4 * (size_t)(P.cls[c].count + 1), "pu"});
     }
     std::sort(tv.begin(), tv.end(), [](const Interval& a, const Interval& c) { return a.lo < c.lo; });
@@ -231,9 +263,11 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
     for (int c = 0; c < kNumClasses; ++c) {
         const ClassPlan& C = P.cls[c];
         EXPECT(memcmp(img.data() + C.off_pupd, C.pupd.data(), 4 * (size_t)(C.count + 1)) == 0);
+        EXPECT(memcmp(img.data() + C.off_ptri, C.ptri.data(), 4 * (size_t)(C.count + 1)) == 0);
+        EXPECT(memcmp(img.data() + C.off_pgram, C.pgram.data(), 4 * (size_t)(C.count + 1)) == 0);
         if (c == kF32 || C.count == 0) continue;
-        check_split(C.xs_gram, C.total_gram, cus, c == kLarge);
-        check_split(C.xs_poly, C.total_gram, cus, c == kLarge);
+        check_split(C.xs_gram, C.total_gram, cus, c == kLarge && !C.gram_split);
+        check_split(C.xs_poly, C.total_tri, cus, c == kLarge);
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
     const std::vector<int> sm = split_matrices(P);
@@ -297,6 +331,30 @@ int main(int argc, char** argv) {
         EXPECT(make_plan(b.mats.data(), n, &b.hp, false, 0, cus, Q) == MUON_OK && Q.total == P.total);
     }
     for (int t = 0; t < 200; ++t) check_rejections(rng);
+    // gram_splits on its own: the per-head shape (64 tiles of 112 slabs) and c1's block
+    {
+        std::vector<int32_t> S = gram_splits(std::vector<int32_t>(64, 1), std::vector<int32_t>(64, 112), 256);
+        for (int32_t v : S) EXPECT(v == 4);
+        S = gram_splits(std::vector<int32_t>(64, 1), std::vector<int32_t>(64, 112), 512);
+        for (int32_t v : S) EXPECT(v == 8);
+        std::vector<int32_t> tiles = {10, 10, 10, 10, 10, 10, 10}, slabs = {64, 64, 64, 16, 16, 16, 16};
+        S = gram_splits(tiles, slabs, 256);
+        for (int32_t v : S) EXPECT(v == 1);   // 70 tiles: more than a quarter of the slots
+        tiles = {10, 10, 10, 10, 10};
+        slabs = {64, 64, 64, 16, 16};
+        S = gram_splits(tiles, slabs, 256);
+        int64_t tasks = 0;
+        for (size_t k = 0; k < S.size(); ++k) tasks += tiles[k] * S[k];
+        EXPECT(tasks <= 256 && S[0] > 1 && S[0] == S[1] && S[3] >= 1);
+        S = gram_splits(std::vector<int32_t>(2, 136), std::vector<int32_t>(2, 64), 256);
+        EXPECT(S[0] == 1 && S[1] == 1);   // 272 tiles: no split
+        S = gram_splits(std::vector<int32_t>(1, 136), std::vector<int32_t>(1, 64), 256);
+        EXPECT(S[0] == 1);                // 2 parts would take two rounds
+        S = gram_splits(std::vector<int32_t>(3, 1), std::vector<int32_t>(3, 7), 256);
+        for (int32_t v : S) EXPECT(v == 1);   // shorter than a part
+        S = gram_splits(std::vector<int32_t>(1, 1), std::vector<int32_t>(1, 16384), 256);
+        EXPECT(S[0] == kMaxSplit);
+    }
     // xcd_split on its own: degenerate inputs
     {
         const int32_t none[3] = {0, 0, 0};

@@ -181,3 +181,18 @@ def test_config4_hybrid_decoder_two_steps():
 def test_headline_workload():
     wl = synth.headline()
     _run(wl, 1, [0, 7], report_name="headline")
+
+
+def test_perhead_workload():
+    # 64 heads x 128 x 7168 (row blocks of one 8192 x 7168 query projection):
+    # the 128-tile class with a K-split Gram (64 tiles of K = 7168 for 256
+    # compute units); heads sampled at both ends and where the scheduler's
+    # per-XCD ranges start or end
+    wl = synth.perhead()
+    _run(wl, 1, [0, 1, 31, 63], report_name="perhead", split_limit=12)
+
+
+def test_perhead_mixed_workload():
+    # per-head Q and K blocks (128 x 4096) beside whole 4096 x 4096 V and O
+    wl = synth.perhead_mixed()
+    _run(wl, 1, [0, 33, 64, 65], report_name="perhead-mixed")

@@ -177,6 +177,28 @@ def test_step_mixed_batch_f32():
     _run_and_compare(MIXED, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=12)
 
 
+@pytest.mark.parametrize("shapes", [
+    [(128, 7168)] * 3,                                   # small class, 3 tiles: 16 parts each
+    [(1024, 4096), (1024, 1024), (4096, 1024)],          # large class, unequal K
+    [(256, 20000), (100, 3000), (129, 129), (7, 9)],     # both classes split, plus fp32 tiny
+    [(512, 65536)],                                      # one long matrix: 3 tiles x 16 parts
+])
+def test_k_split_gram_launches(shapes):
+    # Gram launches with fewer tiles than compute units run K-split (fp32
+    # partial tiles, then a reduce launch that sums them in part order,
+    # scales, rounds and mirrors); outputs against the oracle as usual, and
+    # the whole step is bitwise repeatable
+    _run_and_compare(shapes, BASE_HP, TOL_O_BF16, seed=77)
+    res = []
+    for _ in range(2):
+        W, G, M = _rand_matrix_inputs(*shapes[0], 5)
+        O = torch.empty_like(W)
+        run_muon_step([mu.muon_matrix(W, G, M, update_out=O)], hp_from(BASE_HP))
+        torch.cuda.synchronize()
+        res.append(O.clone())
+    assert torch.equal(res[0], res[1])
+
+
 @pytest.mark.parametrize("ns_dtype", ["bf16", "fp32"])
 def test_strided_views_leave_the_rest_untouched(ns_dtype):
     # Column slices of wider buffers: param, grad and momentum each with its
