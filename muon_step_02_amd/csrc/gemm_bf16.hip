@@ -514,7 +514,15 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
 __device__ __forceinline__ bool xcd_task(const XcdSplit& xs, int& tile, int& quarter) {
     const int b = (int)blockIdx.x;
     const int x = b & 7;
-    const int t = b >> 3;
+    int t = b >> 3;
+    const int full = xs.rounds * xs.cus;  // 0 unless interleaved
+    if (t < full) {
+        const int r = t / xs.cus;
+        tile = (8 * r + x) * xs.cus + (t - r * xs.cus);
+        quarter = -1;
+        return true;
+    }
+    t -= full;
     const int whole = xs.b[x + 1] - xs.b[x] - xs.sub[x];
     if (t < whole) {
         tile = xs.b[x] + t;

@@ -103,24 +103,36 @@ struct EwGroups {
 };
 
 // Workgroups of a grouped GEMM launch are dealt to the 8 XCDs round-robin
-// (workgroup b runs on XCD b % 8).  XcdSplit gives XCD x the contiguous tile
-// range [b[x], b[x+1]): tiles that share operand slabs then share one L2, and
-// the ranges are cut at equal work (tiles weighted by their K), not equal
-// tile counts.
+// (workgroup b runs on XCD b % 8, as its task b / 8).  An XCD runs its tasks
+// in rounds of one tile per compute unit (`cus` of them).  Two ways of
+// dealing tiles to XCDs:
 //
-// An XCD runs its tiles in rounds of one tile per CU.  When the last round
-// would leave at least half of the CUs idle, its sub[x] tiles are run as
-// four quarter tiles each instead (task order: whole tiles, then the quarters
-// of the remaining tiles, four consecutive tasks per tile).  The grid is
-// 8 * per workgroups, per = the largest task count of an XCD.
+//   ranges (interleaved == 0): XCD x takes the contiguous tile range
+//     [b[x], b[x+1]), cut at equal work (tiles weighted by their K), so the
+//     tiles that share operand slabs share one L2;
+//   interleaved rounds (interleaved == 1): the first `rounds` rounds deal
+//     chunks of `cus` consecutive tiles to the XCDs in turn (XCD x, round r:
+//     chunk 8 r + x), so in each round the 8 XCDs work on neighbouring tiles
+//     of the same matrices and the operand panels they share come from the
+//     memory-side cache instead of HBM; the remaining tiles are split into 8
+//     contiguous parts [b[x], b[x+1]).
+//
+// In both, when the last round of an XCD would leave at least half of its
+// compute units idle, its sub[x] tiles are run as four quarter tiles each
+// (task order: whole tiles, then the quarters of the remaining tiles, four
+// consecutive tasks per tile).  The grid is 8 * per workgroups, per = the
+// largest task count of an XCD.
 struct XcdSplit {
     int32_t b[9];
     int32_t per;
     int32_t sub[8];
+    int32_t interleaved;
+    int32_t rounds;  // interleaved: full rounds dealt chunk by chunk
+    int32_t cus;     // compute units per XCD (chunk length)
 };
-// Split `ntiles[k]` tiles of weight `weight[k]` (matrix order) into 8 ranges;
-// with `quarters`, the short last round of each range is split as above
-// (cus = compute units per XCD).
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters);
+// Deal `ntiles[k]` tiles of weight `weight[k]` (matrix order) to the 8 XCDs
+// as above; `quarters` allows the quarter tiles of a short last round.
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters,
+                   int interleaved = 0);
 
 }  // namespace muon

@@ -111,8 +111,38 @@ struct Interval {
     const char* what;
 };
 
+// The kernels' mapping of workgroup b to (tile, quarter), restated for the
+// check (gemm_bf16.hip, xcd_task): false means no task.
+static bool task_of(const XcdSplit& xs, int b, int& tile, int& quarter) {
+    const int x = b & 7;
+    int t = b >> 3;
+    const int full = xs.rounds * xs.cus;
+    if (t < full) {
+        const int r = t / xs.cus;
+        tile = (8 * r + x) * xs.cus + (t - r * xs.cus);
+        quarter = -1;
+        return true;
+    }
+    t -= full;
+    const int whole = xs.b[x + 1] - xs.b[x] - xs.sub[x];
+    if (t < whole) {
+        tile = xs.b[x] + t;
+        quarter = -1;
+        return true;
+    }
+    const int u = t - whole;
+    if (u >= 4 * xs.sub[x]) return false;
+    tile = xs.b[x] + whole + (u >> 2);
+    quarter = u & 3;
+    return true;
+}
+
+// every tile is computed exactly once: by one whole task or by its four
+// quarters; no task outside [0, total); the grid covers every task
 static void check_split(const XcdSplit& xs, int total, int cus, int quarters) {
-    EXPECT(xs.b[0] == 0 && xs.b[8] == total);
+    EXPECT(xs.b[8] == total && xs.cus == cus);
+    if (!xs.interleaved) EXPECT(xs.b[0] == 0 && xs.rounds == 0);
+    else EXPECT(xs.b[0] == xs.rounds * 8 * cus);
     int per = 0;
     for (int x = 0; x < 8; ++x) {
         const int T = xs.b[x + 1] - xs.b[x];
@@ -120,9 +150,24 @@ static void check_split(const XcdSplit& xs, int total, int cus, int quarters) {
         const int R = T % cus;
         const int want = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
         EXPECT(xs.sub[x] == want);
-        per = std::max(per, T + 3 * xs.sub[x]);
+        per = std::max(per, xs.rounds * cus + T + 3 * xs.sub[x]);
+        if (xs.interleaved) EXPECT(T <= (total - xs.rounds * 8 * cus) / 8 + 1);
     }
     EXPECT(per == xs.per);
+    std::vector<int> whole(total, 0), quarter_mask(total, 0);
+    for (int b = 0; b < 8 * std::max(xs.per, 1); ++b) {
+        int tile, q;
+        if (!task_of(xs, b, tile, q)) continue;
+        EXPECT(tile >= 0 && tile < total);
+        if (tile < 0 || tile >= total) continue;
+        if (q < 0) ++whole[tile];
+        else {
+            EXPECT(!(quarter_mask[tile] & (1 << q)));
+            quarter_mask[tile] |= 1 << q;
+        }
+    }
+    for (int t = 0; t < total; ++t)
+        EXPECT((whole[t] == 1 && quarter_mask[t] == 0) || (whole[t] == 0 && quarter_mask[t] == 15));
 }
 
 static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
@@ -267,6 +312,7 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         EXPECT(memcmp(img.data() + C.off_pgram, C.pgram.data(), 4 * (size_t)(C.count + 1)) == 0);
         if (c == kF32 || C.count == 0) continue;
         check_split(C.xs_gram, C.total_gram, cus, c == kLarge && !C.gram_split);
+        EXPECT(C.xs_gram.interleaved == 1 && C.xs_poly.interleaved == 0 && C.xs_upd.interleaved == 1);
         check_split(C.xs_poly, C.total_tri, cus, c == kLarge);
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
@@ -357,17 +403,45 @@ int main(int argc, char** argv) {
     }
     // xcd_split on its own: degenerate inputs
     {
-        const int32_t none[3] = {0, 0, 0};
-        const int64_t w[3] = {1, 5, 0};
-        XcdSplit xs = xcd_split(none, w, 3, 32, 1);
-        check_split(xs, 0, 32, 1);
-        const int32_t one[1] = {1};
-        xs = xcd_split(one, w, 1, 32, 1);
-        check_split(xs, 1, 32, 1);
-        const int32_t zw[2] = {7, 9};
-        const int64_t zero[2] = {0, 0};
-        xs = xcd_split(zw, zero, 2, 3, 0);
-        check_split(xs, 16, 3, 0);
+        for (int il = 0; il < 2; ++il) {
+            const int32_t none[3] = {0, 0, 0};
+            const int64_t w[3] = {1, 5, 0};
+            XcdSplit xs = xcd_split(none, w, 3, 32, 1, il);
+            check_split(xs, 0, 32, 1);
+            const int32_t one[1] = {1};
+            xs = xcd_split(one, w, 1, 32, 1, il);
+            check_split(xs, 1, 32, 1);
+            const int32_t zw[2] = {7, 9};
+            const int64_t zero[2] = {0, 0};
+            xs = xcd_split(zw, zero, 2, 3, 0, il);
+            check_split(xs, 16, 3, 0);
+            // the 8 x 4096^2 update (2048 tiles) and Gram (1088 tiles)
+            const int32_t upd[8] = {256, 256, 256, 256, 256, 256, 256, 256};
+            const int32_t tri[8] = {136, 136, 136, 136, 136, 136, 136, 136};
+            const int64_t k[8] = {4096, 4096, 4096, 4096, 4096, 4096, 4096, 4096};
+            xs = xcd_split(upd, k, 8, 32, 1, il);
+            check_split(xs, 2048, 32, 1);
+            EXPECT(xs.per == 256);
+            xs = xcd_split(tri, k, 8, 32, 1, il);
+            check_split(xs, 1088, 32, 1);
+            EXPECT(xs.per == 128 + 4 * 8);  // four rounds, then 8 tiles as 32 quarters
+        }
+        // random tile lists in both modes
+        std::mt19937_64 r2(99);
+        for (int t = 0; t < 3000; ++t) {
+            const int n = 1 + (int)(r2() % 12);
+            std::vector<int32_t> tl(n);
+            std::vector<int64_t> wl(n);
+            int total = 0;
+            for (int k = 0; k < n; ++k) {
+                tl[k] = (int32_t)(r2() % (t % 3 ? 700 : 5));
+                wl[k] = 1 + (int64_t)(r2() % 256);
+                total += tl[k];
+            }
+            const int cus = t % 2 ? 32 : 1 + (int)(r2() % 40);
+            const int q = (t >> 1) & 1, il = (t >> 2) & 1;
+            check_split(xcd_split(tl.data(), wl.data(), n, cus, q, il), total, cus, q);
+        }
     }
     if (failures) {
         printf("%d failures\n", failures);

@@ -181,8 +181,9 @@ XCD_SPLIT_TEST = r"""
 #include <vector>
 #include <algorithm>
 namespace muon {
-struct XcdSplit { int32_t b[9]; int32_t per; int32_t sub[8]; };
-XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters);
+struct XcdSplit { int32_t b[9]; int32_t per; int32_t sub[8]; int32_t interleaved, rounds, cus; };
+XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus, int quarters,
+                   int interleaved);
 }
 int main() {
     srand(7);
@@ -198,7 +199,7 @@ int main() {
             w[k] = 1 + rand() % 256;
             total_t += t[k]; total_w += t[k] * w[k]; wmax = std::max(wmax, w[k]);
         }
-        muon::XcdSplit xs = muon::xcd_split(t.data(), w.data(), n, cus, quarters);
+        muon::XcdSplit xs = muon::xcd_split(t.data(), w.data(), n, cus, quarters, 0);
         if (xs.b[0] != 0 || xs.b[8] != total_t) { printf("bad ends %d\n", trial); return 1; }
         int per = 0;
         for (int x = 0; x < 8; ++x) {
