@@ -32,7 +32,7 @@
  * enqueue work and return; they never wait for the device.  muon_step_batched
  * carries its descriptor table (one 216-byte entry per matrix plus prefix
  * arrays) into the caller's workspace in the arguments of small upload
- * kernels, 2 KB per launch (about one launch per 9 matrices), so no host
+ * kernels, 16 KB per launch (about one launch per 70 matrices), so no host
  * memory is referenced after the call returns.
  *
  * Errors: every call validates all of its arguments before it enqueues

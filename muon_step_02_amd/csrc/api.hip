@@ -2,9 +2,9 @@
 // plan.cpp), the AdamW entry points, timing and the test hooks.
 //
 // One call of muon_step_batched enqueues, on the caller's stream:
-//   the descriptor-table upload: ceil(table bytes / 2 KB) launches; the table
-//     holds one 216-byte descriptor per matrix plus the prefix arrays, so
-//     about one launch per 9 matrices;
+//   the descriptor-table upload: ceil(table bytes / 16 KB) launches; the
+//     table holds one 216-byte descriptor per matrix plus the prefix arrays,
+//     so about one launch per 70 matrices;
 //   momentum: one launch per elementwise tile kind in use (at most 3);
 //   norm finalize: one launch;
 //   ns_steps x {gram, poly, update}: one grouped launch per size class in use

@@ -11,8 +11,8 @@
 //   poly:   B = b A + c A A
 //   update: X <- s (a X + B X), X^T alongside
 //
-// ("About Muon: Why Not Adam", kiungsong.github.io, section "Making It
-// Actually Run", and the forty-line listing's iteration.)
+// ("About Muon: Why Not Adam", kiungsong.github.io, sections "Making It
+// Actually Run" and "The whole thing, in about forty lines".)
 #include "muon_internal.h"
 
 namespace muon {

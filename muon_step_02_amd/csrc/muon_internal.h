@@ -67,8 +67,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // All return hipGetLastError() after the launch.
 
 // Copy `bytes` (a multiple of 4) of host data to device memory `dst` in
-// kernel arguments, kTableChunkWords words per launch.
-constexpr int kTableChunkWords = 512;
+// kernel arguments, kTableChunkWords words (16 KB) per launch.  Measured on
+// the MI355X: a 2 KB argument block takes 3.4 us a launch, 16 KB 7.5 us.
+constexpr int kTableChunkWords = 4096;
 hipError_t launch_table_upload(const void* host, size_t bytes, void* dst, hipStream_t st);
 hipError_t launch_momentum(const MatDesc* d, int n, const EwGroups& g, float mu, int nesterov,
                            hipStream_t st);

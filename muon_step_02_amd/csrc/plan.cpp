@@ -122,48 +122,52 @@ XcdSplit xcd_split(const int32_t* ntiles, const int64_t* weight, int n, int cus,
     const int C = cus > 0 ? cus : 1;
     xs.cus = C;
     xs.interleaved = interleaved ? 1 : 0;
-    xs.rounds = 0;
     int64_t total_t = 0;
     for (int k = 0; k < n; ++k) total_t += ntiles[k];
-    if (interleaved) {
-        // full rounds chunk by chunk, the rest in 8 near-equal contiguous parts
-        const int64_t R = total_t / (8 * C);
-        const int64_t rem = total_t - R * 8 * C;
-        const int64_t base = rem / 8, extra = rem % 8;
-        xs.rounds = (int32_t)R;
-        for (int x = 0; x < 8; ++x)
-            xs.b[x] = (int32_t)(R * 8 * C + x * base + (x < extra ? x : extra));
-    } else {
-        int64_t total_w = 0;
-        for (int k = 0; k < n; ++k) total_w += (int64_t)ntiles[k] * (weight[k] > 0 ? weight[k] : 1);
-        // boundary x: first tile whose preceding work reaches x/8 of the total
-        xs.b[0] = 0;
-        int x = 1;
-        int64_t cum_w = 0, cum_t = 0;
-        for (int k = 0; k < n && x < 8; ++k) {
-            const int64_t w = weight[k] > 0 ? weight[k] : 1;
-            const int64_t end_w = cum_w + (int64_t)ntiles[k] * w;
-            while (x < 8 && end_w * 8 >= (int64_t)x * total_w) {
-                // smallest t in [0, ntiles] with (cum_w + t*w) * 8 >= x * total_w
-                const int64_t need = (int64_t)x * total_w - cum_w * 8;
-                int64_t t = need <= 0 ? 0 : (need + 8 * w - 1) / (8 * w);
-                if (t > ntiles[k]) t = ntiles[k];
-                PLAN_CHECK(x >= 1 && x < 9);
-                xs.b[x++] = (int32_t)(cum_t + t);
-            }
-            cum_w = end_w;
-            cum_t += ntiles[k];
+    // interleaved: the full rounds are dealt chunk by chunk; the tiles after
+    // them, like every tile in range mode, are cut into 8 ranges of equal work
+    const int64_t R = interleaved ? total_t / (8 * C) : 0;
+    const int64_t skip = R * 8 * C;
+    xs.rounds = (int32_t)R;
+    int64_t total_w = 0;
+    {
+        int64_t cum_t = 0;
+        for (int k = 0; k < n; ++k) {
+            const int64_t first = std::max<int64_t>(skip, cum_t), last = cum_t + ntiles[k];
+            if (last > first) total_w += (last - first) * (weight[k] > 0 ? weight[k] : 1);
+            cum_t = last;
         }
-        while (x < 9) xs.b[x++] = (int32_t)total_t;
     }
+    // boundary x: first tile whose preceding work (after `skip`) reaches x/8 of the total
+    xs.b[0] = (int32_t)skip;
+    int x = 1;
+    int64_t cum_w = 0, cum_t = 0;
+    for (int k = 0; k < n && x < 8; ++k) {
+        const int64_t w = weight[k] > 0 ? weight[k] : 1;
+        const int64_t first = std::max<int64_t>(skip, cum_t), last = cum_t + ntiles[k];
+        cum_t = last;
+        if (last <= first) continue;
+        const int64_t cnt = last - first;
+        const int64_t end_w = cum_w + cnt * w;
+        while (x < 8 && end_w * 8 >= (int64_t)x * total_w) {
+            // smallest t in [0, cnt] with (cum_w + t*w) * 8 >= x * total_w
+            const int64_t need = (int64_t)x * total_w - cum_w * 8;
+            int64_t t = need <= 0 ? 0 : (need + 8 * w - 1) / (8 * w);
+            if (t > cnt) t = cnt;
+            PLAN_CHECK(x >= 1 && x < 9);
+            xs.b[x++] = (int32_t)(first + t);
+        }
+        cum_w = end_w;
+    }
+    while (x < 9) xs.b[x++] = (int32_t)total_t;
     xs.b[8] = (int32_t)total_t;
     xs.per = 0;
     for (int i = 0; i < 8; ++i) {
         if (xs.b[i + 1] < xs.b[i]) xs.b[i + 1] = xs.b[i];
         const int T = xs.b[i + 1] - xs.b[i];
         // last round of R tiles on C CUs: as 4R quarter tiles when R <= C/2
-        const int R = T % C;
-        xs.sub[i] = (quarters && R > 0 && 2 * R <= C) ? R : 0;
+        const int Rr = T % C;
+        xs.sub[i] = (quarters && Rr > 0 && 2 * Rr <= C) ? Rr : 0;
         const int tasks = xs.rounds * C + T + 3 * xs.sub[i];
         if (tasks > xs.per) xs.per = tasks;
     }

@@ -142,7 +142,7 @@ static bool task_of(const XcdSplit& xs, int b, int& tile, int& quarter) {
 static void check_split(const XcdSplit& xs, int total, int cus, int quarters) {
     EXPECT(xs.b[8] == total && xs.cus == cus);
     if (!xs.interleaved) EXPECT(xs.b[0] == 0 && xs.rounds == 0);
-    else EXPECT(xs.b[0] == xs.rounds * 8 * cus);
+    else EXPECT(xs.b[0] == xs.rounds * 8 * cus && xs.rounds == total / (8 * cus));
     int per = 0;
     for (int x = 0; x < 8; ++x) {
         const int T = xs.b[x + 1] - xs.b[x];
@@ -151,7 +151,6 @@ static void check_split(const XcdSplit& xs, int total, int cus, int quarters) {
         const int want = (quarters && R > 0 && 2 * R <= cus) ? R : 0;
         EXPECT(xs.sub[x] == want);
         per = std::max(per, xs.rounds * cus + T + 3 * xs.sub[x]);
-        if (xs.interleaved) EXPECT(T <= (total - xs.rounds * 8 * cus) / 8 + 1);
     }
     EXPECT(per == xs.per);
     std::vector<int> whole(total, 0), quarter_mask(total, 0);
@@ -440,7 +439,22 @@ int main(int argc, char** argv) {
             }
             const int cus = t % 2 ? 32 : 1 + (int)(r2() % 40);
             const int q = (t >> 1) & 1, il = (t >> 2) & 1;
-            check_split(xcd_split(tl.data(), wl.data(), n, cus, q, il), total, cus, q);
+            const XcdSplit xs = xcd_split(tl.data(), wl.data(), n, cus, q, il);
+            check_split(xs, total, cus, q);
+            // the ranges after the interleaved rounds hold equal work, within one tile
+            std::vector<int64_t> tw;
+            int64_t wmax = 1;
+            for (int k = 0; k < n; ++k) {
+                for (int i = 0; i < tl[k]; ++i) tw.push_back(wl[k]);
+                wmax = std::max(wmax, wl[k]);
+            }
+            int64_t tail_w = 0;
+            for (int i = xs.b[0]; i < total; ++i) tail_w += tw[i];
+            for (int x = 0; x < 8; ++x) {
+                int64_t w = 0;
+                for (int i = xs.b[x]; i < xs.b[x + 1]; ++i) w += tw[i];
+                EXPECT(w * 8 <= tail_w + 8 * wmax);
+            }
         }
     }
     if (failures) {
