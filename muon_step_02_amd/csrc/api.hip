@@ -243,7 +243,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
             e = timed(h, 2, s, [&] {
-                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, s)
+                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, C.kmax_n, s)
                                  : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall,
                                                     C.gram_split, s);
             });
@@ -256,9 +256,12 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
+            Prefix pp = pc[k];  // the polynomial's own tiling (128-tiles when poly_small)
+            pp.tri = reinterpret_cast<const int32_t*>(ws + C.off_ppoly);
             e = timed(h, 3, s, [&] {
-                return k == kF32 ? launch_poly_f32(dc, C.count, pc[k], C.total_tri, b, c, s)
-                                 : launch_poly_bf16(dc, C.count, pc[k], C.xs_poly, a, b, c, k == kSmall, s);
+                return k == kF32 ? launch_poly_f32(dc, C.count, pp, C.total_poly, C.kmax_m, b, c, s)
+                                 : launch_poly_bf16(dc, C.count, pp, C.xs_poly, a, b, c,
+                                                    k == kSmall || C.poly_small, s);
             });
         }
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
@@ -266,7 +269,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
             e = timed(h, 4, s, [&] {
-                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, a, s)
+                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, C.kmax_m, a, s)
                                  : launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, s);
             });
         }

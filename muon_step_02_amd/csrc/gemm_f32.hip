@@ -23,73 +23,56 @@ enum { GRAM = 0, POLY = 1, UPDATE = 2 };
 constexpr int T = kTileF32;  // 64
 constexpr int KS = 16;
 
+// Tile of phase PHASE: operands, their leading dimensions and the K extent.
 template <int PHASE>
-__global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__ descs, int n,
-                                                     const int32_t* __restrict__ prefix, int it,
-                                                     float ca, float cb, float cc) {
-    __shared__ float Ps[KS][T + 4];
-    __shared__ float Qs[KS][T + 4];
-    const int tile = blockIdx.x;
-    const int mi = find_matrix(prefix, n, tile);
-    const MatDesc& d = descs[mi];
-    const int lt = tile - prefix[mi];
-    const int64_t mp = d.mp, np = d.np;
-    const int tcols = (int)((PHASE == UPDATE ? np : mp) / T);
-    const int ti = lt / tcols, tj = lt - ti * tcols;
-
+struct F32Tile {
+    const MatDesc* d;
     const float* P;
     const float* Q;
     int64_t ldp, ldq;
     int K;
+    int ti, tj;
+};
+
+template <int PHASE>
+__device__ __forceinline__ F32Tile<PHASE> f32_tile(const MatDesc* __restrict__ descs, int n,
+                                                   const int32_t* __restrict__ prefix, int it) {
+    F32Tile<PHASE> t;
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    t.d = &descs[mi];
+    const MatDesc& d = *t.d;
+    const int lt = tile - prefix[mi];
+    const int tcols = (int)((PHASE == UPDATE ? d.np : d.mp) / T);
+    t.ti = lt / tcols;
+    t.tj = lt - t.ti * tcols;
     if (PHASE == GRAM) {
-        P = Q = reinterpret_cast<const float*>(d.x[it & 1]);
-        ldp = ldq = np;
-        K = (int)np;
+        t.P = t.Q = reinterpret_cast<const float*>(d.x[it & 1]);
+        t.ldp = t.ldq = d.np;
+        t.K = (int)d.np;
     } else if (PHASE == POLY) {
-        P = Q = reinterpret_cast<const float*>(d.a);
-        ldp = ldq = mp;
-        K = (int)mp;
+        t.P = t.Q = reinterpret_cast<const float*>(d.a);
+        t.ldp = t.ldq = d.mp;
+        t.K = (int)d.mp;
     } else {
-        P = reinterpret_cast<const float*>(d.b);
-        Q = reinterpret_cast<const float*>(d.xt[it & 1]);
-        ldp = ldq = mp;
-        K = (int)mp;
+        t.P = reinterpret_cast<const float*>(d.b);
+        t.Q = reinterpret_cast<const float*>(d.xt[it & 1]);
+        t.ldp = t.ldq = d.mp;
+        t.K = (int)d.mp;
     }
-    const int t = threadIdx.x;
-    const int ty = t >> 4, tx = t & 15;
-    const int lrow = t >> 2, lk = (t & 3) * 4;
-    const float* Pr = P + (int64_t)(ti * T + lrow) * ldp + lk;
-    const float* Qr = Q + (int64_t)(tj * T + lrow) * ldq + lk;
+    return t;
+}
 
-    float acc[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-
-    for (int k0 = 0; k0 < K; k0 += KS) {
-        const float4 pv = gld(reinterpret_cast<const float4*>(Pr + k0));
-        const float4 qv = gld(reinterpret_cast<const float4*>(Qr + k0));
-        __syncthreads();
-        Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
-        Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = Ps[kk][ty * 4 + r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = Qs[kk][tx * 4 + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
-        }
-    }
-
-    const int64_t i0 = (int64_t)ti * T + ty * 4;
-    const int64_t j0 = (int64_t)tj * T + tx * 4;
+// Epilogue of a 64 x 64 tile: thread (ty, tx) holds rows 4 ty .. 4 ty + 3,
+// columns 4 tx .. 4 tx + 3 of the product.
+template <int PHASE>
+__device__ __forceinline__ void f32_epilogue(const F32Tile<PHASE>& t, const float (&acc)[4][4], int it,
+                                             float ca, float cb, float cc) {
+    const MatDesc& d = *t.d;
+    const int ty = threadIdx.x >> 4, tx = threadIdx.x & 15;
+    const int64_t mp = d.mp, np = d.np;
+    const int64_t i0 = (int64_t)t.ti * T + ty * 4;
+    const int64_t j0 = (int64_t)t.tj * T + tx * 4;
     if (PHASE == GRAM) {
         const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
         const float s2 = s * s;
@@ -131,23 +114,134 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__
     }
 }
 
+// K in slabs of KS through LDS (any K, a multiple of KS).
+template <int PHASE>
+__global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__ descs, int n,
+                                                     const int32_t* __restrict__ prefix, int it,
+                                                     float ca, float cb, float cc) {
+    __shared__ float Ps[KS][T + 4];
+    __shared__ float Qs[KS][T + 4];
+    const F32Tile<PHASE> tl = f32_tile<PHASE>(descs, n, prefix, it);
+    const int t = threadIdx.x;
+    const int ty = t >> 4, tx = t & 15;
+    const int lrow = t >> 2, lk = (t & 3) * 4;
+    const float* Pr = tl.P + (int64_t)(tl.ti * T + lrow) * tl.ldp + lk;
+    const float* Qr = tl.Q + (int64_t)(tl.tj * T + lrow) * tl.ldq + lk;
+
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+
+    for (int k0 = 0; k0 < tl.K; k0 += KS) {
+        const float4 pv = gld(reinterpret_cast<const float4*>(Pr + k0));
+        const float4 qv = gld(reinterpret_cast<const float4*>(Qr + k0));
+        __syncthreads();
+        Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
+        Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = Ps[kk][ty * 4 + r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = Qs[kk][tx * 4 + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
+        }
+    }
+    f32_epilogue<PHASE>(tl, acc, it, ca, cb, cc);
+}
+
+// K of at most KMAX: every thread issues the loads of the tile's whole K
+// extent at once, they go to LDS transposed, and after one barrier the
+// product runs from LDS.  The slab loop above waits for one load latency per
+// 16 K-steps; on a small matrix that chain, not the arithmetic, sets the
+// launch time.
+template <int PHASE, int KMAX>
+__global__ __launch_bounds__(256) void ns_f32_shortk_kernel(const MatDesc* __restrict__ descs, int n,
+                                                            const int32_t* __restrict__ prefix, int it,
+                                                            float ca, float cb, float cc) {
+    static_assert(KMAX % KS == 0, "whole slabs");
+    __shared__ float Ps[KMAX][T + 4];
+    __shared__ float Qs[KMAX][T + 4];
+    const F32Tile<PHASE> tl = f32_tile<PHASE>(descs, n, prefix, it);
+    const int t = threadIdx.x;
+    const int ty = t >> 4, tx = t & 15;
+    const int lrow = t >> 2, lk = (t & 3) * 4;
+    const float* Pr = tl.P + (int64_t)(tl.ti * T + lrow) * tl.ldp + lk;
+    const float* Qr = tl.Q + (int64_t)(tl.tj * T + lrow) * tl.ldq + lk;
+    constexpr int NSL = KMAX / KS;
+    float4 pv[NSL], qv[NSL];
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+        if (s * KS < tl.K) {
+            pv[s] = gld(reinterpret_cast<const float4*>(Pr + s * KS));
+            qv[s] = gld(reinterpret_cast<const float4*>(Qr + s * KS));
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+        if (s * KS < tl.K) {
+            const int k = s * KS + lk;
+            Ps[k + 0][lrow] = pv[s].x; Ps[k + 1][lrow] = pv[s].y; Ps[k + 2][lrow] = pv[s].z; Ps[k + 3][lrow] = pv[s].w;
+            Qs[k + 0][lrow] = qv[s].x; Qs[k + 1][lrow] = qv[s].y; Qs[k + 2][lrow] = qv[s].z; Qs[k + 3][lrow] = qv[s].w;
+        }
+    }
+    __syncthreads();
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    for (int k0 = 0; k0 < tl.K; k0 += KS) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = Ps[k0 + kk][ty * 4 + r];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = Qs[k0 + kk][tx * 4 + c];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
+        }
+    }
+    f32_epilogue<PHASE>(tl, acc, it, ca, cb, cc);
+}
+
 }  // namespace
 
-hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st) {
-    ns_f32_kernel<GRAM><<<total, 256, 0, st>>>(d, n, p.gram, it, 0.f, 0.f, 0.f);
+// The kernel for a launch whose largest K is kmax.
+template <int PHASE>
+hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total, int it, int kmax,
+                      float a, float b, float c, hipStream_t st) {
+    if (kmax <= 64)
+        ns_f32_shortk_kernel<PHASE, 64><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+    else if (kmax <= 256)
+        ns_f32_shortk_kernel<PHASE, 256><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+    else
+        ns_f32_kernel<PHASE><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
     return hipGetLastError();
 }
 
-hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, hipStream_t st) {
+    return launch_f32<GRAM>(d, n, p.gram, total, it, kmax, 0.f, 0.f, 0.f, st);
+}
+
+hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, int kmax, float b, float c,
                            hipStream_t st) {
-    ns_f32_kernel<POLY><<<total, 256, 0, st>>>(d, n, p.tri, 0, 0.f, b, c);
-    return hipGetLastError();
+    return launch_f32<POLY>(d, n, p.tri, total, 0, kmax, 0.f, b, c, st);
 }
 
-hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, float a,
+hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, float a,
                              hipStream_t st) {
-    ns_f32_kernel<UPDATE><<<total, 256, 0, st>>>(d, n, p.upd, it, a, 0.f, 0.f);
-    return hipGetLastError();
+    return launch_f32<UPDATE>(d, n, p.upd, total, it, kmax, a, 0.f, 0.f, st);
 }
 
 }  // namespace muon

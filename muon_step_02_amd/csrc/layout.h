@@ -90,7 +90,9 @@ struct MatDesc {
 // task t is part t / tiles of tile t % tiles).
 struct Prefix {
     const int32_t* gram;  // Gram tasks (tiles, or tiles * gram_split when split)
-    const int32_t* tri;   // triangle tiles (polynomial; reduce of a split Gram)
+    const int32_t* tri;   // triangle tiles: the reduce of a split Gram, and the
+                          // polynomial (of a large-class launch that runs on
+                          // 128-tiles, the triangle of those)
     const int32_t* upd;   // update tiles
 };
 

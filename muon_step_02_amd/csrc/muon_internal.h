@@ -88,16 +88,22 @@ hipError_t launch_gram_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& x
 hipError_t launch_gram_reduce_bf16(const MatDesc* d, int n, Prefix p, int tiles, int it, int small,
                                    hipStream_t st);
 // poly writes B = a I + b A + c A A, so the update is the plain product B X
+// small: 128-tiles (the small class, or a large-class launch with few
+// 256-tiles), else 256-tiles
 hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, float a,
                             float b, float c, int small, hipStream_t st);
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                               int small, hipStream_t st);
 
-// fp32 class (every tile of the symmetric products; p.gram == p.tri)
-hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, hipStream_t st);
-hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, float b, float c,
+// fp32 class (every tile of the symmetric products; p.gram == p.tri).
+// kmax: the largest K of the launch's matrices (n' for the Gram, m' for the
+// polynomial and the update); up to 256 the whole K extent of a tile is
+// staged in LDS at once
+hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax,
                            hipStream_t st);
-hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, float a,
+hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, int kmax, float b, float c,
+                           hipStream_t st);
+hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, float a,
                              hipStream_t st);
 
 // single-phase test hooks (one matrix, caller buffers)
@@ -108,8 +114,10 @@ hipError_t launch_poly_bf16_single(const void* A, void* B, int m, int64_t lda, f
 hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int m, int n,
                                      int64_t ldx, int64_t ldb, float s, int cus, hipStream_t st);
 
-// AdamW: tensors travel in kernel arguments, kAdamwGroup per launch.
-constexpr int kAdamwGroup = 32;
+// AdamW: tensors travel in kernel arguments, kAdamwGroup per launch (about
+// 12 KB of arguments; a launch per 32 tensors cost a model's many small norm
+// and bias tensors about 16 us each, launch gap included).
+constexpr int kAdamwGroup = 256;
 struct AdamwGroup {
     void* param[kAdamwGroup];
     const void* grad[kAdamwGroup];
@@ -122,6 +130,7 @@ struct AdamwGroup {
     uint8_t vec4[kAdamwGroup];
     int32_t count;
 };
+static_assert(sizeof(AdamwGroup) <= 16384, "AdamW group must fit a 16 KB argument block");
 constexpr int kAdamwChunk = 4096;  // elements per workgroup
 hipError_t launch_adamw(const AdamwGroup& g, int total_blocks, float lr, float beta1, float beta2,
                         float eps, float wd, float bc1, float bc2, const float* gscale,

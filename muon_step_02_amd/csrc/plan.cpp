@@ -213,6 +213,7 @@ std::vector<int32_t> gram_splits(const std::vector<int32_t>& tiles,
 // all matrices, one launch per tile kind, each with a prefix array of its own.
 muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bool need_ptrs,
                       uintptr_t ws, int cus, Plan& P) {
+    P = Plan{};  // nothing carries over from an earlier plan in P
     if (!mats || n < 1) return MUON_ERR_INVALID_ARG;
     muon_status st = check_hparams(hp);
     if (st != MUON_OK) return st;
@@ -251,6 +252,7 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         first += count[c];
         C.pgram.assign(C.count + 1, 0);
         C.ptri.assign(C.count + 1, 0);
+        C.ppoly.assign(C.count + 1, 0);
         C.pupd.assign(C.count + 1, 0);
     }
     int64_t tew = 0, tek[kNumEwKinds] = {0, 0, 0};
@@ -319,6 +321,8 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         P.pew[k + 1] = (int32_t)tew;
         for (int kk = 0; kk < kNumEwKinds; ++kk) P.pek[kk][k + 1] = (int32_t)tek[kk];
         const int kc = k - P.cls[c].first;
+        P.cls[c].kmax_n = std::max<int>(P.cls[c].kmax_n, d.np);
+        P.cls[c].kmax_m = std::max<int>(P.cls[c].kmax_m, d.mp);
         P.cls[c].ptri[kc + 1] = (int32_t)tgram[c];
         P.cls[c].pupd[kc + 1] = (int32_t)tupd[c];
     }
@@ -349,6 +353,29 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
             C.pgram[k + 1] = (int32_t)tasks;
         }
         C.total_gram = (int)tasks;
+        // The polynomial of a large-class launch whose 256-tiles fill at most
+        // half the compute units (every XCD would run them as quarter tiles,
+        // one workgroup per compute unit, four slots per tile) runs on the
+        // triangle of 128-tiles instead, two workgroups per compute unit, when
+        // those fit one round: the 128-triangle skips the upper quarter of
+        // each diagonal tile.  (d=1024 block: 70 tiles of 256 as 280 quarter
+        // slots over 256 CUs against 252 tiles of 128 in one round.)
+        std::vector<int32_t> tp(tg);
+        if (c == kLarge && C.count > 0 && 2 * (int64_t)C.total_tri <= 8 * (int64_t)cus) {
+            int64_t t128 = 0;
+            for (int k = 0; k < C.count; ++k) {
+                const int64_t T = P.d[C.first + k].mp / kClassTile[kSmall];
+                t128 += T * (T + 1) / 2;
+            }
+            C.poly_small = t128 <= 2 * 8 * (int64_t)cus;
+        }
+        if (C.poly_small)
+            for (int k = 0; k < C.count; ++k) {
+                const int64_t T = P.d[C.first + k].mp / kClassTile[kSmall];
+                tp[k] = (int32_t)(T * (T + 1) / 2);
+            }
+        for (int k = 0; k < C.count; ++k) C.ppoly[k + 1] = C.ppoly[k] + tp[k];
+        C.total_poly = C.ppoly[C.count];
         if (c == kF32 || C.count == 0) continue;
         // tile work = k-steps: the Gram runs over n' (a part of it when
         // split), the polynomial and the update over m'
@@ -366,7 +393,7 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         // ranges (each measured faster that way on the 8 x 4096^2 and the
         // 192-matrix MoE workloads)
         C.xs_gram = xcd_split(tk.data(), wn.data(), C.count, cus, C.gram_split ? 0 : quarters, 1);
-        C.xs_poly = xcd_split(tg.data(), wm.data(), C.count, cus, quarters, 0);
+        C.xs_poly = xcd_split(tp.data(), wm.data(), C.count, cus, C.poly_small ? 0 : quarters, 0);
         C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters, 1);
     }
 
@@ -379,6 +406,8 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         P.cls[c].off_pgram = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
         P.cls[c].off_ptri = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+        P.cls[c].off_ppoly = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
         P.cls[c].off_pupd = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
@@ -436,8 +465,10 @@ void table_image(const Plan& P, std::vector<char>& out) {
         PLAN_CHECK(c.off_pgram + (size_t)(c.count + 1) * 4 <= P.table_bytes);
         PLAN_CHECK(c.off_pupd + (size_t)(c.count + 1) * 4 <= P.table_bytes);
         PLAN_CHECK(c.off_ptri + (size_t)(c.count + 1) * 4 <= P.table_bytes);
+        PLAN_CHECK(c.off_ppoly + (size_t)(c.count + 1) * 4 <= P.table_bytes);
         memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_ptri, c.ptri.data(), (size_t)(c.count + 1) * 4);
+        memcpy(hb + c.off_ppoly, c.ppoly.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
     }
 }
@@ -448,7 +479,7 @@ std::vector<int> split_matrices(const Plan& P) {
         const ClassPlan& C = P.cls[c];
         if (C.count == 0) continue;
         const XcdSplit* splits[3] = {&C.xs_gram, &C.xs_poly, &C.xs_upd};
-        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.ptri, &C.pupd};
+        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.ppoly, &C.pupd};
         for (int s = 0; s < 3; ++s) {
             const XcdSplit& xs = *splits[s];
             const std::vector<int32_t>& pre = *prefixes[s];

@@ -17,10 +17,12 @@ namespace muon {
 // Tiles and launch ranges of one size class.
 struct ClassPlan {
     int first = 0, count = 0;           // descriptor range [first, first + count)
-    std::vector<int32_t> pgram, ptri, pupd;      // count + 1 entries each (see Prefix)
-    size_t off_pgram = 0, off_ptri = 0, off_pupd = 0;  // their offsets in the workspace
-    int total_gram = 0, total_tri = 0, total_upd = 0;
+    std::vector<int32_t> pgram, ptri, ppoly, pupd;  // count + 1 entries each (see Prefix)
+    size_t off_pgram = 0, off_ptri = 0, off_ppoly = 0, off_pupd = 0;  // their workspace offsets
+    int total_gram = 0, total_tri = 0, total_poly = 0, total_upd = 0;
     bool gram_split = false;            // the Gram launch runs K-split (bf16 classes)
+    bool poly_small = false;            // large class: the polynomial runs on 128-tiles
+    int kmax_n = 0, kmax_m = 0;         // largest padded n' and m' of the class
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };
 

@@ -183,6 +183,7 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
     // classes: contiguous, in class order, descending work inside
     int64_t ew_run = 0, ek_run[kNumEwKinds] = {0, 0, 0};
     int64_t g_run[kNumClasses] = {0, 0, 0}, u_run[kNumClasses] = {0, 0, 0};
+    int64_t p_run[kNumClasses] = {0, 0, 0};
     EXPECT(P.pew[0] == 0);
     std::vector<Interval> iv;
     iv.push_back({ws, ws + P.table_bytes, "table"});
@@ -231,6 +232,15 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         u_run[d.cls] += (d.mp / tile) * (d.np / tile);
         const int kc = k - C.first;
         EXPECT(C.ptri[kc + 1] == g_run[d.cls] && C.pupd[kc + 1] == u_run[d.cls]);
+        // polynomial tiles: the triangle, or the triangle of 128-tiles
+        if (C.poly_small) {
+            EXPECT(d.cls == kLarge && d.mp % kClassTile[kSmall] == 0);
+            const int64_t T = d.mp / kClassTile[kSmall];
+            p_run[d.cls] += T * (T + 1) / 2;
+        } else {
+            p_run[d.cls] += d.cls == kF32 ? Ts * Ts : Ts * (Ts + 1) / 2;
+        }
+        EXPECT(C.ppoly[kc + 1] == p_run[d.cls]);
         // Gram tasks: the triangle tiles, times the K-parts when the class splits
         const int64_t tri = C.ptri[kc + 1] - C.ptri[kc];
         EXPECT(d.gram_split >= 1 && d.gram_split <= kMaxSplit);
@@ -284,6 +294,28 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         tv.push_back({P.off_pek[kind], P.off_pek[kind] + 4 * (size_t)(n + 1), "pek"});
     for (int c = 0; c < kNumClasses; ++c) {
         EXPECT(P.cls[c].total_tri == g_run[c] && P.cls[c].total_upd == u_run[c]);
+        EXPECT(P.cls[c].total_poly == p_run[c]);
+        {
+            int kn = 0, km = 0;
+            for (int k = P.cls[c].first; k < P.cls[c].first + P.cls[c].count; ++k) {
+                kn = std::max<int>(kn, P.d[k].np);
+                km = std::max<int>(km, P.d[k].mp);
+            }
+            EXPECT(P.cls[c].kmax_n == kn && P.cls[c].kmax_m == km);
+        }
+        // 128-tiles for the polynomial exactly when the 256-tiles fill at most
+        // half the compute units and the 128-tiles fit one round at two per unit
+        if (c == kLarge && P.cls[c].count > 0) {
+            int64_t t128 = 0;
+            for (int k = P.cls[c].first; k < P.cls[c].first + P.cls[c].count; ++k) {
+                const int64_t T = P.d[k].mp / kClassTile[kSmall];
+                t128 += T * (T + 1) / 2;
+            }
+            const bool want = 2 * (int64_t)P.cls[c].total_tri <= 8 * (int64_t)cus && t128 <= 16 * (int64_t)cus;
+            EXPECT(P.cls[c].poly_small == want);
+        } else {
+            EXPECT(!P.cls[c].poly_small);
+        }
         EXPECT(P.cls[c].total_gram == P.cls[c].pgram[P.cls[c].count]);
         // a split launch fits one round; a launch is split only when starved
         if (P.cls[c].gram_split) {
@@ -293,6 +325,7 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         }
         tv.push_back({P.cls[c].off_pgram, P.cls[c].off_pgram + 4 * (size_t)(P.cls[c].count + 1), "pg"});
         tv.push_back({P.cls[c].off_ptri, P.cls[c].off_ptri + 4 * (size_t)(P.cls[c].count + 1), "pt"});
+        tv.push_back({P.cls[c].off_ppoly, P.cls[c].off_ppoly + 4 * (size_t)(P.cls[c].count + 1), "pp"});
         tv.push_back({P.cls[c].off_pupd, P.cls[c].off_pupd + 4 * (size_t)(P.cls[c].count + 1), "pu"});
     }
     std::sort(tv.begin(), tv.end(), [](const Interval& a, const Interval& c) { return a.lo < c.lo; });
@@ -308,11 +341,12 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         const ClassPlan& C = P.cls[c];
         EXPECT(memcmp(img.data() + C.off_pupd, C.pupd.data(), 4 * (size_t)(C.count + 1)) == 0);
         EXPECT(memcmp(img.data() + C.off_ptri, C.ptri.data(), 4 * (size_t)(C.count + 1)) == 0);
+        EXPECT(memcmp(img.data() + C.off_ppoly, C.ppoly.data(), 4 * (size_t)(C.count + 1)) == 0);
         EXPECT(memcmp(img.data() + C.off_pgram, C.pgram.data(), 4 * (size_t)(C.count + 1)) == 0);
         if (c == kF32 || C.count == 0) continue;
         check_split(C.xs_gram, C.total_gram, cus, c == kLarge && !C.gram_split);
         EXPECT(C.xs_gram.interleaved == 1 && C.xs_poly.interleaved == 0 && C.xs_upd.interleaved == 1);
-        check_split(C.xs_poly, C.total_tri, cus, c == kLarge);
+        check_split(C.xs_poly, C.total_poly, cus, c == kLarge && !C.poly_small);
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
     const std::vector<int> sm = split_matrices(P);
@@ -399,6 +433,52 @@ int main(int argc, char** argv) {
         for (int32_t v : S) EXPECT(v == 1);   // shorter than a part
         S = gram_splits(std::vector<int32_t>(1, 1), std::vector<int32_t>(1, 16384), 256);
         EXPECT(S[0] == kMaxSplit);
+    }
+    // the polynomial's tiling on workloads whose launch shapes are known
+    {
+        auto plan_of = [&](const std::vector<std::pair<int64_t, int64_t>>& shapes, Plan& P) {
+            Batch b;
+            uintptr_t next = (uintptr_t)1 << 40;
+            for (const auto& sh : shapes) {
+                muon_matrix m;
+                memset(&m, 0, sizeof(m));
+                m.rows = sh.first;
+                m.cols = sh.second;
+                m.param_dtype = m.grad_dtype = MUON_F32;
+                m.ld_param = m.ld_grad = m.ld_mom = m.cols;
+                const size_t bytes = (size_t)(m.rows * m.cols) * 4 + 4096;
+                m.param = (void*)next;
+                next += bytes;
+                m.grad = (const void*)next;
+                next += bytes;
+                m.momentum = (float*)next;
+                next += bytes;
+                b.mats.push_back(m);
+            }
+            memset(&b.hp, 0, sizeof(b.hp));
+            b.hp.lr = 2e-4f;
+            b.hp.momentum = 0.95f;
+            b.hp.eps = 1e-7f;
+            b.hp.extra_scale = 1.f;
+            b.hp.nesterov = 1;
+            b.hp.ns_steps = 5;
+            b.hp.ns_dtype = MUON_BF16;
+            const uintptr_t ws = (uintptr_t)1 << 36;
+            EXPECT(make_plan(b.mats.data(), (int)shapes.size(), &b.hp, true, ws, 32, P) == MUON_OK);
+            check_plan(b, P, ws, 32);
+        };
+        Plan P;
+        // d=1024 block: 70 tiles of 256 -> 7 x 36 tiles of 128 in one round
+        plan_of({{1024, 1024}, {1024, 1024}, {1024, 1024}, {1024, 1024}, {4096, 1024}, {4096, 1024},
+                 {1024, 4096}}, P);
+        EXPECT(P.cls[kLarge].poly_small && P.cls[kLarge].total_tri == 70 && P.cls[kLarge].total_poly == 252);
+        EXPECT(P.cls[kLarge].xs_poly.per == 32);
+        // one 4096^2 matrix: 136 tiles fill more than half the units
+        plan_of({{4096, 4096}}, P);
+        EXPECT(!P.cls[kLarge].poly_small && P.cls[kLarge].total_poly == 136);
+        // 105 tiles of 256 (3584^2) would be 420 quarter slots; 406 tiles of 128 fit one round
+        plan_of({{3584, 3584}}, P);
+        EXPECT(P.cls[kLarge].poly_small && P.cls[kLarge].total_poly == 406);
     }
     // xcd_split on its own: degenerate inputs
     {

@@ -599,7 +599,10 @@ ADAMW_HP = dict(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
                                      (torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16)])
 def test_adamw_many_tensors_three_steps(pdt, gdt):
     h = Handle.get()
-    sizes = [1, 3, 4095, 4096, 4097, 10000, 65539, 0] + [257 * k for k in range(1, 33)]
+    # more tensors than one launch takes (256): two launch groups, the second
+    # starting inside the run of small tensors
+    sizes = ([1, 3, 4095, 4096, 4097, 10000, 65539, 0] + [257 * k for k in range(1, 33)] +
+             [5 + 37 * (k % 11) for k in range(240)])
     g = torch.Generator(device=DEV).manual_seed(5)
     P, M, V, ref = [], [], [], []
     for n in sizes:

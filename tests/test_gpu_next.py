@@ -141,7 +141,9 @@ ADAMW_HP = dict(lr=2e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 def test_adamw_global_norm_clipping(scale, gdt):
     h = Handle.get()
     g = torch.Generator(device=DEV).manual_seed(21)
-    sizes = [3, 4096, 70000, 1024 * 1024 + 5] + [999] * 35
+    # 279 tensors: two launch groups (256 tensors each at most), so the sum of
+    # squares of the second group lands after the first group's partials
+    sizes = [3, 4096, 70000, 1024 * 1024 + 5] + [999] * 35 + [777] * 240
     P = [torch.randn(n, generator=g, device=DEV) * 0.02 for n in sizes]
     Ms = [torch.zeros(n, device=DEV) for n in sizes]
     Vs = [torch.zeros(n, device=DEV) for n in sizes]

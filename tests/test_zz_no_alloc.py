@@ -33,7 +33,7 @@ def _copy(st):
 @pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16])
 def test_noalloc_equals_workspace_entry_point_twice(gdt):
     h = Handle.get()
-    calls = [([3, 4096, 70000, 1 << 20, 4097] + [999] * 40, 1),   # 1.1 M elements, 45 tensors
+    calls = [([3, 4096, 70000, 1 << 20, 4097] + [999] * 260, 1),  # 1.3 M elements, 265 tensors
              ([5000, 12345, 1], 2)]                               # smaller: 3 tensors
     for sizes, step in calls:
         a = _state(sizes, 10 + step, gdt)
