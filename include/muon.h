@@ -198,7 +198,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                               size_t workspace_bytes, void* stream);
 
 /* One AdamW step over n tensors on `stream`.  No workspace: the tensor list
- * travels in kernel arguments (groups of at most 32 tensors per launch).
+ * travels in kernel arguments (groups of at most 256 tensors per launch).
  * Rejects n < 1, numel < 0, null pointers for numel > 0, unknown dtypes,
  * step < 1. */
 muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n,

@@ -115,8 +115,8 @@ hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int
                                      int64_t ldx, int64_t ldb, float s, int cus, hipStream_t st);
 
 // AdamW: tensors travel in kernel arguments, kAdamwGroup per launch (about
-// 12 KB of arguments; a launch per 32 tensors cost a model's many small norm
-// and bias tensors about 16 us each, launch gap included).
+// 12 KB of arguments), so a model's many small norm and bias tensors share a
+// launch: each extra launch costs about 16 us, launch gap included.
 constexpr int kAdamwGroup = 256;
 struct AdamwGroup {
     void* param[kAdamwGroup];
