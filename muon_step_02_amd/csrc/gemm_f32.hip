@@ -3,9 +3,10 @@
 // Same three products and the same buffer layout as the bf16 kernels (X and
 // X^T kept side by side, padded to multiples of 64, zero padding), computed
 // with fp32 FMAs on 64 x 64 tiles: 256 threads, 4 x 4 outputs each, K in
-// slabs of 16 staged through LDS.  This path serves small matrices where
-// accuracy matters more than throughput, so every tile of the symmetric
-// outputs is computed (no triangle skipping).
+// slabs of 16 staged through LDS, or, when every matrix of a launch has K of
+// at most 256, the whole K extent staged at once.  This path serves small
+// matrices where accuracy matters more than throughput, so every tile of the
+// symmetric outputs is computed (no triangle skipping).
 //
 //   gram:   A = s^2 X X^T        (s = 1/(||Y||+eps) on the first iteration)
 //   poly:   B = b A + c A A
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(256) void ns_f32_shortk_kernel(const MatDesc* __res
 
 }  // namespace
 
-// The kernel for a launch whose largest K is kmax.
+// The kernel for a launch whose largest K is kmax (the planner's largest n'
+// or m' of the class, so every tile's K fits the chosen KMAX).
 template <int PHASE>
 hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total, int it, int kmax,
                       float a, float b, float c, hipStream_t st) {
