@@ -33,7 +33,15 @@
  * carries its descriptor table (one 216-byte entry per matrix plus prefix
  * arrays) into the caller's workspace in the arguments of small upload
  * kernels, 16 KB per launch (about one launch per 70 matrices), so no host
- * memory is referenced after the call returns.
+ * memory is referenced after the call returns.  A handle owns one more
+ * stream (default priority).  Matrices fall in three size classes with launches
+ * of their own: short side above 128; short side 33 to 128; and the fp32
+ * iteration (every matrix under MUON_F32, short side at most 32 under
+ * MUON_BF16).  When a call uses more than one class, the Newton-Schulz
+ * launches of every class but the first in use run on that stream, ordered
+ * after the caller's stream by an event and joined back into it by another
+ * before the call's last launch.  For the caller the
+ * call still behaves as work on its own stream, stream capture included.
  *
  * Errors: every call validates all of its arguments before it enqueues
  * anything.  Any status other than MUON_ERR_HIP means nothing was enqueued.

@@ -8,7 +8,10 @@
 //   momentum: one launch per elementwise tile kind in use (at most 3);
 //   norm finalize: one launch;
 //   ns_steps x {gram, poly, update}: one grouped launch per size class in use
-//     (at most 3) and phase, plus a reduce launch after a K-split Gram;
+//     (at most 3) and phase, plus a reduce launch after a K-split Gram; with
+//     more than one class in use, the classes other than the large one go on
+//     the handle's second stream, forked from the caller's stream after the
+//     norms and joined back into it before the apply (an event each);
 //   apply: one launch per elementwise tile kind in use.
 #include <math.h>
 #include <string.h>
@@ -39,6 +42,11 @@ struct muon_context {
     int device = 0;
     float* scratch = nullptr;  // this device's copy of `scratch` (below), device address
     int cus_per_xcd = 32;  // compute units per XCD (tile rounds)
+    // second stream (default priority) for the Newton-Schulz launches of the
+    // size classes other than the large one, forked from and joined back into
+    // the caller's stream with two events
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
     std::vector<char> table;  // host image of the descriptor table (reused)
     bool profiling = false;
     std::vector<TimedLaunch> timed;     // recorded since the last collect
@@ -162,7 +170,13 @@ muon_status muon_init(int device, muon_handle* out) {
     if (!h) return MUON_ERR_HIP;
     h->device = device;
     h->cus_per_xcd = prop.multiProcessorCount >= 8 ? prop.multiProcessorCount / 8 : 1;
-    if (resolve_scratch(device, &h->scratch) != hipSuccess) {
+    if (resolve_scratch(device, &h->scratch) != hipSuccess ||
+        hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess) {
+        if (h->join) (void)hipEventDestroy(h->join);
+        if (h->fork) (void)hipEventDestroy(h->fork);
+        if (h->side) (void)hipStreamDestroy(h->side);
         delete h;
         return MUON_ERR_HIP;
     }
@@ -179,6 +193,10 @@ muon_status muon_destroy(muon_handle h) {
         h->event_pool.push_back(t.stop);
     }
     for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
+    (void)hipStreamSynchronize(h->side);
+    (void)hipEventDestroy(h->join);
+    (void)hipEventDestroy(h->fork);
+    (void)hipStreamDestroy(h->side);
     delete h;
     return MUON_OK;
 }
@@ -230,6 +248,21 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
 
     hipError_t e = timed(h, 0, s, [&] { return launch_momentum(dd, n, eg, hp->momentum, hp->nesterov, s); });
     if (e == hipSuccess) e = timed(h, 1, s, [&] { return launch_norm_finalize(dd, n, hp->eps, s); });
+    // The Newton-Schulz launches of different size classes read and write
+    // disjoint buffers.  With more than one class in use, every class but the
+    // large one runs on the handle's second stream, forked after the norms and
+    // joined before the apply: their short launches then use compute units
+    // that the large class's launches leave idle in their partial rounds.
+    int used = 0;
+    for (int c = 0; c < kNumClasses; ++c) used += P.cls[c].count > 0 ? 1 : 0;
+    const int primary = P.cls[kLarge].count > 0 ? kLarge : P.cls[kSmall].count > 0 ? kSmall : kF32;
+    const bool forked = used > 1;
+    hipStream_t cs[kNumClasses];
+    for (int c = 0; c < kNumClasses; ++c) cs[c] = (forked && c != primary) ? h->side : s;
+    if (e == hipSuccess && forked) {
+        e = hipEventRecord(h->fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+    }
     for (int it = 0; it < hp->ns_steps && e == hipSuccess; ++it) {
         float a = kMuonA, b = kMuonB, c = kMuonC;
         if (hp->coeffs) {
@@ -237,42 +270,51 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             b = hp->coeffs[3 * it + 1];
             c = hp->coeffs[3 * it + 2];
         }
-        // the classes' launches of one phase are independent of each other
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 2, s, [&] {
-                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, C.kmax_n, s)
+            const hipStream_t sk = cs[k];
+            e = timed(h, 2, sk, [&] {
+                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, C.kmax_n, sk)
                                  : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall,
-                                                    C.gram_split, s);
+                                                    C.gram_split, sk);
             });
             if (e == hipSuccess && C.gram_split)
-                e = timed(h, 2, s, [&] {
-                    return launch_gram_reduce_bf16(dc, C.count, pc[k], C.total_tri, it, k == kSmall, s);
+                e = timed(h, 2, sk, [&] {
+                    return launch_gram_reduce_bf16(dc, C.count, pc[k], C.total_tri, it, k == kSmall, sk);
                 });
         }
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
+            const hipStream_t sk = cs[k];
             Prefix pp = pc[k];  // the polynomial's own tiling (128-tiles when poly_small)
             pp.tri = reinterpret_cast<const int32_t*>(ws + C.off_ppoly);
-            e = timed(h, 3, s, [&] {
-                return k == kF32 ? launch_poly_f32(dc, C.count, pp, C.total_poly, C.kmax_m, b, c, s)
+            e = timed(h, 3, sk, [&] {
+                return k == kF32 ? launch_poly_f32(dc, C.count, pp, C.total_poly, C.kmax_m, b, c, sk)
                                  : launch_poly_bf16(dc, C.count, pp, C.xs_poly, a, b, c,
-                                                    k == kSmall || C.poly_small, s);
+                                                    k == kSmall || C.poly_small, sk);
             });
         }
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
-            e = timed(h, 4, s, [&] {
-                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, C.kmax_m, a, s)
-                                 : launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, s);
+            const hipStream_t sk = cs[k];
+            e = timed(h, 4, sk, [&] {
+                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, C.kmax_m, a, sk)
+                                 : launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }
+    }
+    if (forked) {
+        // joined whatever happened above, so that a capture of the caller's
+        // stream never ends with the second stream still forked
+        hipError_t ej = hipEventRecord(h->join, h->side);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(s, h->join, 0);
+        if (e == hipSuccess) e = ej;
     }
     if (e == hipSuccess)
         e = timed(h, 5, s, [&] {
