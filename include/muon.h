@@ -214,10 +214,12 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n,
 
 /* ---- per-phase timing (benchmarks) ---------------------------------------
  * While enabled, muon_step_batched records a pair of HIP events (on the
- * caller's stream) around every kernel launch it makes, and adamw_step around
- * each of its launches.  muon_profile_collect waits for the last recorded
- * event, adds up the elapsed times per phase since the previous collect (or
- * enable), fills `out` and clears the record.  Timing does not change what the
+ * stream the launch goes to: the caller's, or the handle's second stream)
+ * around every kernel launch it makes, and adamw_step around each of its
+ * launches.  muon_profile_collect waits for every recorded event, adds up the
+ * elapsed times per phase since the previous collect (or enable), fills `out`
+ * and clears the record.  Launches on the two streams may overlap in time,
+ * and their durations are added all the same.  Timing does not change what the
  * kernels compute.  Phases: 0 momentum, 1 norm, 2 gram, 3 poly, 4 update,
  * 5 apply, 6 adamw. */
 #define MUON_NUM_PHASES 7

@@ -517,9 +517,11 @@ muon_status muon_profile_collect(muon_handle h, muon_phase_times* out) {
     DeviceGuard g(h->device);
     memset(out, 0, sizeof(*out));
     muon_status st = MUON_OK;
-    if (!h->timed.empty() && hipEventSynchronize(h->timed.back().stop) != hipSuccess) st = MUON_ERR_HIP;
     for (TimedLaunch& t : h->timed) {
+        // launches may sit on the handle's second stream as well as on the
+        // caller's: wait for each one's own stop event
         float ms = 0.f;
+        if (st == MUON_OK && hipEventSynchronize(t.stop) != hipSuccess) st = MUON_ERR_HIP;
         if (st == MUON_OK && hipEventElapsedTime(&ms, t.start, t.stop) != hipSuccess) st = MUON_ERR_HIP;
         if (t.phase >= 0 && t.phase < MUON_NUM_PHASES) {
             out->ms[t.phase] += ms;
