@@ -191,3 +191,33 @@ def test_adamw_clipping_below_threshold_equals_plain_step():
         mu.adamw_step_clipped(h, tb, hp, 0.0, ws)
     with pytest.raises(mu.MuonError):
         mu.adamw_step_clipped(h, tb, hp, 1.0, ws[:8])
+
+
+def test_mixed_class_call_equals_one_call_per_class():
+    # One call over all three size classes (a 1024 x 768 matrix, four
+    # 128 x 1536 blocks, two tiny matrices running the fp32 iteration) forks
+    # the small and fp32 classes onto the handle's second stream after the
+    # momentum launch and joins them before the apply.  The same matrices in
+    # three calls of one class each (no fork) must give bitwise equal
+    # weights, momenta and orthogonalised updates, over two steps.
+    shapes = [(1024, 768)] + [(128, 1536)] * 4 + [(24, 700), (900, 17)]
+    hp = hp_from(BASE_HP)
+
+    def state():
+        W = [_weight(r, c, 40 + i) for i, (r, c) in enumerate(shapes)]
+        M = [torch.zeros(r, c, device=DEV) for r, c in shapes]
+        O = [torch.empty(r, c, device=DEV) for r, c in shapes]
+        return W, M, O
+
+    (Wa, Ma, Oa), (Wb, Mb, Ob) = state(), state()
+    groups = [[0], [1, 2, 3, 4], [5, 6]]   # large, small, fp32 classes
+    for step in range(2):
+        G = [_grad(r, c, 60 + 10 * step + i) for i, (r, c) in enumerate(shapes)]
+        run_muon_step([mu.muon_matrix(Wa[i], G[i], Ma[i], update_out=Oa[i]) for i in range(len(shapes))], hp)
+        for grp in groups:
+            run_muon_step([mu.muon_matrix(Wb[i], G[i], Mb[i], update_out=Ob[i]) for i in grp], hp)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(Oa[i], Ob[i]), (step, i, "O")
+            assert torch.equal(Ma[i], Mb[i]), (step, i, "M")
+            assert torch.equal(Wa[i], Wb[i]), (step, i, "W")
