@@ -304,8 +304,12 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             const MatDesc* dc = dd + C.first;
             const hipStream_t sk = cs[k];
             e = timed(h, 4, sk, [&] {
-                return k == kF32 ? launch_update_f32(dc, C.count, pc[k], C.total_upd, it, C.kmax_m, a, sk)
-                                 : launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
+                if (k == kF32) return launch_update_f32(dc, C.count, pc[k], C.total_upd, it, C.kmax_m, a, sk);
+                if (C.strip > 0)
+                    return launch_update_strip_bf16(dc, C.count,
+                                                    reinterpret_cast<const int32_t*>(ws + C.off_pstrip),
+                                                    C.xs_strip, it, C.strip, sk);
+                return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }
     }

@@ -316,6 +316,22 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier without a memory fence: the wave's own LDS reads are
+// waited for (lgkmcnt 0, no other counter), then s_barrier; compiler-only
+// fences keep every LDS access on its side.  Global->LDS copies in flight
+// stay in flight (__syncthreads() would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7: lgkmcnt(0) only
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <bool LIGHT>
+__device__ __forceinline__ void epi_barrier() {
+    if constexpr (LIGHT) lds_barrier(); else __syncthreads();
+}
+
 
 // E chunks of one epilogue band, in the order the combine pass reads them.
 template <class C, int QN>
@@ -407,24 +423,37 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
         }
     }
 
-    // Epilogue through LDS, in bands of RB rows: the waves holding the band
-    // write their fp32 accumulators (MFMA 32x32 layout: lane l, register r is
-    // row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
-    // combines 8 consecutive columns with E and stores 16 bytes of the output,
-    // and, for the transposed copy, 8 consecutive rows of one column.
-    //
-    // The band loop is unrolled so the compiler can count outstanding memory
-    // operations exactly: no wait ever covers the stores of earlier bands, and
-    // E is loaded one band ahead so its latency hides behind the LDS work.
     float* sb = reinterpret_cast<float*>(lds_arr(st, 0));
+    wait_vmcnt<0>();  // every slab copy has landed: the band buffer is free
+    epilogue_bands<C, HAS_E, F32OUT>(acc, row0, col0, ep, sb, wm, wn, frow, khalf);
+}
+
+// Epilogue through LDS, in bands of RB rows: the waves holding the band
+// write their fp32 accumulators (MFMA 32x32 layout: lane l, register r is
+// row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
+// combines 8 consecutive columns with E and stores 16 bytes of the output,
+// and, for the transposed copy, 8 consecutive rows of one column.  sb: the
+// fp32 band buffer (RB x BN).
+//
+// The band loop is unrolled so the compiler can count outstanding memory
+// operations exactly: no wait ever covers the stores of earlier bands, and
+// E is loaded one band ahead so its latency hides behind the LDS work.
+// LIGHT: the band barriers carry no memory fence, for a caller that has
+// global->LDS copies in flight into other arrays which the epilogue must not
+// wait for.
+// (wm, wn): the wave's position in the WM x WN grid; frow = lane & 31,
+// khalf = lane >> 5.
+template <class C, bool HAS_E, bool F32OUT, bool LIGHT = false>
+__device__ __forceinline__ void epilogue_bands(const f32x16 (&acc)[C::FM][C::FN], int64_t row0,
+                                               int64_t col0, const Epi& ep, float* sb, int wm,
+                                               int wn, int frow, int khalf) {
     constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
     uint4 ecur[QN], enxt[QN];
-    wait_vmcnt<0>();  // every slab copy has landed: the band buffer is free
     if (HAS_E) load_e_band<C, QN>(ep, row0, col0, 0, ecur);
 #pragma unroll
     for (int band = 0; band < C::BM / C::RB; ++band) {
         if (HAS_E && band + 1 < C::BM / C::RB) load_e_band<C, QN>(ep, row0, col0, band + 1, enxt);
-        __syncthreads();
+        epi_barrier<LIGHT>();
         // the band is MFMA row block i of the waves with wm * TM + 32 i == 32 band
 #pragma unroll
         for (int i = 0; i < C::FM; ++i) {
@@ -440,7 +469,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
                 }
             }
         }
-        __syncthreads();
+        epi_barrier<LIGHT>();
         const int64_t brow = row0 + (int64_t)band * C::RB;
 #pragma unroll
         for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
@@ -485,7 +514,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
             }
         }
         if (!F32OUT && ep.outT) {
-            __syncthreads();
+            epi_barrier<LIGHT>();
 #pragma unroll
             for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
                 const int ch = q * C::NT + threadIdx.x;
@@ -796,6 +825,88 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     }
 }
 
+// Update of the small class in strips.  Its matrices have m' = 128, so B is
+// one 128 x 128 tile and an update tile is B times one 128-column block of X
+// (K = 128: two slabs).  A workgroup takes `strip` consecutive column tiles
+// of one matrix: B's two slabs are copied to LDS once, and the X block of the
+// next tile is copied while the current tile's epilogue runs (its band
+// barriers carry no memory fence, so those copies stay in flight).  One tile
+// per workgroup spent most of its time in the copy latency and the epilogue,
+// one after the other.  LDS: the two stage arrays (B's slab and X's slab of
+// k 0..63 and of k 64..127) and the epilogue's band buffer.
+template <class C>
+__global__ __launch_bounds__(C::NT) void ns_update_strip_kernel(const MatDesc* __restrict__ descs, int n,
+                                                                const int32_t* __restrict__ prefix,
+                                                                XcdSplit xs, int it, int strip) {
+    static_assert(C::BM == 128 && C::BN == 128 && C::NS == 2 && !C::SPLIT && C::BK == 64,
+                  "two stage arrays hold the whole K of 128");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds1[kLdsArr];
+    __shared__ __attribute__((aligned(1024))) float band[C::RB * C::BN];
+    const Stages st{{lds0, lds1, lds1, lds1}};
+    int task, q;
+    if (!xcd_task(xs, task, q)) return;  // no quarter tasks
+    const int mi = find_matrix(prefix, n, task);
+    const MatDesc& d = descs[mi];
+    const int64_t mp = d.mp, np = d.np;  // mp == 128
+    const int tiles = (int)(np / C::BN);
+    const int j0 = (task - prefix[mi]) * strip;
+    const int j1 = min(j0 + strip, tiles);
+    const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+    Epi ep;
+    ep.outF = nullptr;
+    ep.out = reinterpret_cast<uint16_t*>(d.x[(it + 1) & 1]);
+    ep.ld_out = np;
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
+    ep.coef_acc = 1.f;
+    ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
+    ep.diag = 0.f;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
+    constexpr int KS = C::BK / 16;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        load_slab<C, C::BM>(B + u * C::BK, mp, stage_p<C>(st, u), wave, lane);
+        load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)j0 * C::BN, np, stage_q<C>(st, u), wave, lane);
+    }
+    for (int j = j0; j < j1; ++j) {
+        wait_vmcnt<0>();  // B and this tile's X have landed (and the last tile's stores)
+        __syncthreads();
+        f32x16 acc[C::FM][C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                Frags<C> f;
+                read_frags<C, true>(st, u, kk, wm, wn, frow, khalf, lane, f);
+                mfma_frags<C>(acc, f);
+            }
+        }
+        __syncthreads();  // every wave is done with this X block: its slabs may be refilled
+        if (j + 1 < j1) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np, stage_q<C>(st, u),
+                                wave, lane);
+        }
+        epilogue_bands<C, false, false, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow, khalf);
+    }
+}
+
 // single-matrix variants for the test hooks
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
@@ -933,6 +1044,12 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
         ns_update_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, p.upd, xs, it);
     else
         ns_update_kernel<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(d, n, p.upd, xs, it);
+    return hipGetLastError();
+}
+
+hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
+                                   const XcdSplit& xs, int it, int strip, hipStream_t st) {
+    ns_update_strip_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs, it, strip);
     return hipGetLastError();
 }
 

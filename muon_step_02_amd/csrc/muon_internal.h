@@ -94,6 +94,10 @@ hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& x
                             float b, float c, int small, hipStream_t st);
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                               int small, hipStream_t st);
+// the small class's update in strips of `strip` consecutive column tiles per
+// workgroup; prefix_strip: strips per matrix, prefix-summed
+hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
+                                   const XcdSplit& xs, int it, int strip, hipStream_t st);
 
 // fp32 class (every tile of the symmetric products; p.gram == p.tri).
 // kmax: the largest K of the launch's matrices (n' for the Gram, m' for the

@@ -395,6 +395,27 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         C.xs_gram = xcd_split(tk.data(), wn.data(), C.count, cus, C.gram_split ? 0 : quarters, 1);
         C.xs_poly = xcd_split(tp.data(), wm.data(), C.count, cus, C.poly_small ? 0 : quarters, 0);
         C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters, 1);
+        // The small class's update in strips: as many consecutive column
+        // tiles per workgroup as it takes to fill two workgroups per compute
+        // unit once, when that is at least two (one tile per workgroup runs
+        // the copy latency and the epilogue back to back).
+        C.strip = 0;
+        C.pstrip.assign(C.count + 1, 0);
+        if (c == kSmall) {
+            const int64_t slots = 2 * 8 * (int64_t)cus;
+            const int64_t L = ((int64_t)C.total_upd + slots - 1) / slots;
+            if (L >= 2) {
+                C.strip = (int)L;
+                std::vector<int32_t> ts(C.count);
+                std::vector<int64_t> wsz(C.count, L);
+                for (int k = 0; k < C.count; ++k) {
+                    ts[k] = (int32_t)((tu[k] + L - 1) / L);
+                    C.pstrip[k + 1] = C.pstrip[k] + ts[k];
+                }
+                C.total_strips = C.pstrip[C.count];
+                C.xs_strip = xcd_split(ts.data(), wsz.data(), C.count, cus, 0, 0);
+            }
+        }
     }
 
     size_t off = align_up((size_t)n * sizeof(MatDesc), 256);
@@ -408,6 +429,8 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         P.cls[c].off_ptri = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
         P.cls[c].off_ppoly = off;
+        off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
+        P.cls[c].off_pstrip = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
         P.cls[c].off_pupd = off;
         off = align_up(off + (size_t)(P.cls[c].count + 1) * 4, 256);
@@ -469,6 +492,10 @@ void table_image(const Plan& P, std::vector<char>& out) {
         memcpy(hb + c.off_pgram, c.pgram.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_ptri, c.ptri.data(), (size_t)(c.count + 1) * 4);
         memcpy(hb + c.off_ppoly, c.ppoly.data(), (size_t)(c.count + 1) * 4);
+        if (!c.pstrip.empty()) {
+            PLAN_CHECK(c.off_pstrip + (size_t)(c.count + 1) * 4 <= P.table_bytes);
+            memcpy(hb + c.off_pstrip, c.pstrip.data(), (size_t)(c.count + 1) * 4);
+        }
         memcpy(hb + c.off_pupd, c.pupd.data(), (size_t)(c.count + 1) * 4);
     }
 }
@@ -478,8 +505,9 @@ std::vector<int> split_matrices(const Plan& P) {
     for (int c = kLarge; c <= kSmall; ++c) {
         const ClassPlan& C = P.cls[c];
         if (C.count == 0) continue;
-        const XcdSplit* splits[3] = {&C.xs_gram, &C.xs_poly, &C.xs_upd};
-        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.ppoly, &C.pupd};
+        // the update launch deals strips when the class runs it in strips
+        const XcdSplit* splits[3] = {&C.xs_gram, &C.xs_poly, C.strip > 0 ? &C.xs_strip : &C.xs_upd};
+        const std::vector<int32_t>* prefixes[3] = {&C.pgram, &C.ppoly, C.strip > 0 ? &C.pstrip : &C.pupd};
         for (int s = 0; s < 3; ++s) {
             const XcdSplit& xs = *splits[s];
             const std::vector<int32_t>& pre = *prefixes[s];

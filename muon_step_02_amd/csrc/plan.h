@@ -22,6 +22,13 @@ struct ClassPlan {
     int total_gram = 0, total_tri = 0, total_poly = 0, total_upd = 0;
     bool gram_split = false;            // the Gram launch runs K-split (bf16 classes)
     bool poly_small = false;            // large class: the polynomial runs on 128-tiles
+    // small class: the update in strips of `strip` consecutive column tiles
+    // per workgroup (0: one tile per workgroup, the ordinary update launch)
+    int strip = 0;
+    std::vector<int32_t> pstrip;        // strips per matrix, count + 1 entries
+    size_t off_pstrip = 0;
+    int total_strips = 0;
+    XcdSplit xs_strip{};
     int kmax_n = 0, kmax_m = 0;         // largest padded n' and m' of the class
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };

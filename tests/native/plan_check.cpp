@@ -326,6 +326,7 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         tv.push_back({P.cls[c].off_pgram, P.cls[c].off_pgram + 4 * (size_t)(P.cls[c].count + 1), "pg"});
         tv.push_back({P.cls[c].off_ptri, P.cls[c].off_ptri + 4 * (size_t)(P.cls[c].count + 1), "pt"});
         tv.push_back({P.cls[c].off_ppoly, P.cls[c].off_ppoly + 4 * (size_t)(P.cls[c].count + 1), "pp"});
+        tv.push_back({P.cls[c].off_pstrip, P.cls[c].off_pstrip + 4 * (size_t)(P.cls[c].count + 1), "ps"});
         tv.push_back({P.cls[c].off_pupd, P.cls[c].off_pupd + 4 * (size_t)(P.cls[c].count + 1), "pu"});
     }
     std::sort(tv.begin(), tv.end(), [](const Interval& a, const Interval& c) { return a.lo < c.lo; });
@@ -347,6 +348,33 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         check_split(C.xs_gram, C.total_gram, cus, c == kLarge && !C.gram_split);
         EXPECT(C.xs_gram.interleaved == 1 && C.xs_poly.interleaved == 0 && C.xs_upd.interleaved == 1);
         check_split(C.xs_poly, C.total_poly, cus, c == kLarge && !C.poly_small);
+        // the small class's update in strips exactly when two or more tiles per
+        // workgroup fill two workgroups per compute unit once; strips cover
+        // each matrix's column tiles once, in order
+        if (c == kSmall) {
+            const int64_t slots = 16 * (int64_t)cus;
+            const int64_t L = (C.total_upd + slots - 1) / slots;
+            EXPECT(C.strip == (L >= 2 ? (int)L : 0));
+            if (C.strip > 0) {
+                int64_t run = 0;
+                EXPECT(C.pstrip.size() == (size_t)C.count + 1 && C.pstrip[0] == 0);
+                for (int k = 0; k < C.count; ++k) {
+                    const MatDesc& d = P.d[C.first + k];
+                    EXPECT(d.mp == kClassTile[kSmall]);
+                    const int64_t tiles = d.np / kClassTile[kSmall];
+                    EXPECT(tiles == C.pupd[k + 1] - C.pupd[k]);
+                    run += (tiles + C.strip - 1) / C.strip;
+                    EXPECT(C.pstrip[k + 1] == run);
+                    // the last strip of the matrix is not empty
+                    EXPECT((int64_t)(C.pstrip[k + 1] - C.pstrip[k] - 1) * C.strip < tiles);
+                }
+                EXPECT(C.total_strips == run);
+                check_split(C.xs_strip, C.total_strips, cus, 0);
+                EXPECT(memcmp(img.data() + C.off_pstrip, C.pstrip.data(), 4 * (size_t)(C.count + 1)) == 0);
+            }
+        } else {
+            EXPECT(C.strip == 0);
+        }
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
     const std::vector<int> sm = split_matrices(P);
@@ -479,6 +507,15 @@ int main(int argc, char** argv) {
         // 105 tiles of 256 (3584^2) would be 420 quarter slots; 406 tiles of 128 fit one round
         plan_of({{3584, 3584}}, P);
         EXPECT(P.cls[kLarge].poly_small && P.cls[kLarge].total_poly == 406);
+        // per head: 64 blocks of 128 x 7168 (56 column tiles each) in strips of 7
+        plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 7168}), P);
+        EXPECT(P.cls[kSmall].strip == 7 && P.cls[kSmall].total_strips == 512);
+        // 16 blocks of 100 x 4900 (39 tiles each): strips of 2, the last one short
+        plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
+        EXPECT(P.cls[kSmall].strip == 2 && P.cls[kSmall].total_strips == 16 * 20);
+        // few small tiles: one tile per workgroup
+        plan_of({{128, 4096}, {100, 3000}}, P);
+        EXPECT(P.cls[kSmall].strip == 0);
     }
     // xcd_split on its own: degenerate inputs
     {
