@@ -275,11 +275,14 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
             if (C.count == 0) continue;
             const MatDesc* dc = dd + C.first;
             const hipStream_t sk = cs[k];
-            e = timed(h, 2, sk, [&] {
-                return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, C.kmax_n, sk)
-                                 : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall,
-                                                    C.gram_split, sk);
-            });
+            // from the second iteration on, a fused class's Gram parts come
+            // from the previous update's strips: only the reduce remains
+            if (!(C.fuse_gram && it > 0))
+                e = timed(h, 2, sk, [&] {
+                    return k == kF32 ? launch_gram_f32(dc, C.count, pc[k], C.total_gram, it, C.kmax_n, sk)
+                                     : launch_gram_bf16(dc, C.count, pc[k], C.xs_gram, it, k == kSmall,
+                                                        C.gram_split, sk);
+                });
             if (e == hipSuccess && C.gram_split)
                 e = timed(h, 2, sk, [&] {
                     return launch_gram_reduce_bf16(dc, C.count, pc[k], C.total_tri, it, k == kSmall, sk);
@@ -308,7 +311,8 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                 if (C.strip > 0)
                     return launch_update_strip_bf16(dc, C.count,
                                                     reinterpret_cast<const int32_t*>(ws + C.off_pstrip),
-                                                    C.xs_strip, it, C.strip, sk);
+                                                    C.xs_strip, it, C.strip,
+                                                    C.fuse_gram && it + 1 < hp->ns_steps, sk);
                 return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }

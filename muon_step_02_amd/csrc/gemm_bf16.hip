@@ -346,6 +346,124 @@ __device__ __forceinline__ void load_e_band(const Epi& ep, int64_t row0, int64_t
     }
 }
 
+// Epilogue through LDS, in bands of RB rows: the waves holding the band
+// write their fp32 accumulators (MFMA 32x32 layout: lane l, register r is
+// row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
+// combines 8 consecutive columns with E and stores 16 bytes of the output,
+// and, for the transposed copy, 8 consecutive rows of one column.  sb: the
+// fp32 band buffer (RB x BN).
+//
+// The band loop is unrolled so the compiler can count outstanding memory
+// operations exactly: no wait ever covers the stores of earlier bands, and
+// E is loaded one band ahead so its latency hides behind the LDS work.
+// LIGHT: the band barriers carry no memory fence, for a caller that has
+// global->LDS copies in flight into other arrays which the epilogue must not
+// wait for.  XO: the stored bf16 tile is also written to LDS as two row
+// slabs of 64 columns each (xo[0], xo[1]; layout of load_slab), for a
+// product of the tile with itself.
+// (wm, wn): the wave's position in the WM x WN grid; frow = lane & 31,
+// khalf = lane >> 5.
+template <class C, bool HAS_E, bool F32OUT, bool LIGHT = false, bool XO = false>
+__device__ __forceinline__ void epilogue_bands(const f32x16 (&acc)[C::FM][C::FN], int64_t row0,
+                                               int64_t col0, const Epi& ep, float* sb, int wm,
+                                               int wn, int frow, int khalf,
+                                               uint16_t* const* xo = nullptr) {
+    static_assert(!XO || (C::BN == 128 && C::BK == 64 && !F32OUT), "two 64-column slabs");
+    constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
+    uint4 ecur[QN], enxt[QN];
+    if (HAS_E) load_e_band<C, QN>(ep, row0, col0, 0, ecur);
+#pragma unroll
+    for (int band = 0; band < C::BM / C::RB; ++band) {
+        if (HAS_E && band + 1 < C::BM / C::RB) load_e_band<C, QN>(ep, row0, col0, band + 1, enxt);
+        epi_barrier<LIGHT>();
+        // the band is MFMA row block i of the waves with wm * TM + 32 i == 32 band
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            if (wm * C::TM + i * 32 == band * C::RB) {
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int c = wn * C::TN + j * 32 + frow;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3);
+                        sb[sbi<C>(rr, c)] = acc[i][j][r];
+                    }
+                }
+            }
+        }
+        epi_barrier<LIGHT>();
+        const int64_t brow = row0 + (int64_t)band * C::RB;
+#pragma unroll
+        for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
+            const int ch = q * C::NT + threadIdx.x;
+            const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
+            const float4 a0 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8));
+            const float4 a1 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8) + 4);
+            float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            if (HAS_E) {
+                const uint32_t ew[4] = {ecur[q].x, ecur[q].y, ecur[q].z, ecur[q].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w = ew[e >> 1];
+                    const float xe = __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+                    v[e] = ep.post * (ep.coef_acc * v[e] + ep.coef_e * xe);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = ep.post * (ep.coef_acc * v[e]);
+            }
+            if (ep.diag != 0.f) {
+                const int64_t dc = brow + rr - (col0 + c8);  // column of the diagonal, relative
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] += (dc == e) ? ep.diag : 0.f;
+            }
+            if constexpr (F32OUT) {
+                // a partial tile of a K-split Gram: fp32, tile-local, no mirror
+                float* o = ep.outF + (int64_t)(band * C::RB + rr) * C::BN + c8;
+                gst(reinterpret_cast<float4*>(o), make_float4(v[0], v[1], v[2], v[3]));
+                gst(reinterpret_cast<float4*>(o + 4), make_float4(v[4], v[5], v[6], v[7]));
+                continue;
+            }
+            uint4 o;
+            o.x = pack2(v[0], v[1]);
+            o.y = pack2(v[2], v[3]);
+            o.z = pack2(v[4], v[5]);
+            o.w = pack2(v[6], v[7]);
+            store_out(ep.out + brow * ep.ld_out + col0, (uint32_t)(rr * ep.ld_out + c8) * 2u, o);
+            if constexpr (XO) {
+                const int row = band * C::RB + rr;
+                const int lch = (c8 & 63) >> 3;
+                *reinterpret_cast<uint4*>(xo[c8 >> 6] + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3)) = o;
+            }
+            if (ep.outT) {
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+        if (!F32OUT && ep.outT) {
+            epi_barrier<LIGHT>();
+#pragma unroll
+            for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
+                const int ch = q * C::NT + threadIdx.x;
+                const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sb[sbi<C>(i8 + e, c)];
+                uint4 o;
+                o.x = pack2(v[0], v[1]);
+                o.y = pack2(v[2], v[3]);
+                o.z = pack2(v[4], v[5]);
+                o.w = pack2(v[6], v[7]);
+                store_out(ep.outT + col0 * ep.ld_outT + brow, (uint32_t)(c * ep.ld_outT + i8) * 2u, o);
+            }
+        }
+        if (HAS_E) {
+#pragma unroll
+            for (int q = 0; q < QN; ++q) ecur[q] = enxt[q];
+        }
+    }
+}
+
 // C tile = sum_k P[i][k] Q'[k][j] for the BM rows starting at P0 (leading
 // dimension ldp) and BN columns of Q' (K a multiple of BK), then the
 // epilogue.  Q' is read as Q'[k][j] = Q0[j * ldq + k] (NT) or, with QKN, as
@@ -426,115 +544,6 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ P0, int64
     float* sb = reinterpret_cast<float*>(lds_arr(st, 0));
     wait_vmcnt<0>();  // every slab copy has landed: the band buffer is free
     epilogue_bands<C, HAS_E, F32OUT>(acc, row0, col0, ep, sb, wm, wn, frow, khalf);
-}
-
-// Epilogue through LDS, in bands of RB rows: the waves holding the band
-// write their fp32 accumulators (MFMA 32x32 layout: lane l, register r is
-// row (r & 3) + 4*(l >> 5) + 8*(r >> 2), column l & 31); then every thread
-// combines 8 consecutive columns with E and stores 16 bytes of the output,
-// and, for the transposed copy, 8 consecutive rows of one column.  sb: the
-// fp32 band buffer (RB x BN).
-//
-// The band loop is unrolled so the compiler can count outstanding memory
-// operations exactly: no wait ever covers the stores of earlier bands, and
-// E is loaded one band ahead so its latency hides behind the LDS work.
-// LIGHT: the band barriers carry no memory fence, for a caller that has
-// global->LDS copies in flight into other arrays which the epilogue must not
-// wait for.
-// (wm, wn): the wave's position in the WM x WN grid; frow = lane & 31,
-// khalf = lane >> 5.
-template <class C, bool HAS_E, bool F32OUT, bool LIGHT = false>
-__device__ __forceinline__ void epilogue_bands(const f32x16 (&acc)[C::FM][C::FN], int64_t row0,
-                                               int64_t col0, const Epi& ep, float* sb, int wm,
-                                               int wn, int frow, int khalf) {
-    constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
-    uint4 ecur[QN], enxt[QN];
-    if (HAS_E) load_e_band<C, QN>(ep, row0, col0, 0, ecur);
-#pragma unroll
-    for (int band = 0; band < C::BM / C::RB; ++band) {
-        if (HAS_E && band + 1 < C::BM / C::RB) load_e_band<C, QN>(ep, row0, col0, band + 1, enxt);
-        epi_barrier<LIGHT>();
-        // the band is MFMA row block i of the waves with wm * TM + 32 i == 32 band
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-            if (wm * C::TM + i * 32 == band * C::RB) {
-#pragma unroll
-                for (int j = 0; j < C::FN; ++j) {
-                    const int c = wn * C::TN + j * 32 + frow;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int rr = 8 * (r >> 2) + 4 * khalf + (r & 3);
-                        sb[sbi<C>(rr, c)] = acc[i][j][r];
-                    }
-                }
-            }
-        }
-        epi_barrier<LIGHT>();
-        const int64_t brow = row0 + (int64_t)band * C::RB;
-#pragma unroll
-        for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
-            const int ch = q * C::NT + threadIdx.x;
-            const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
-            const float4 a0 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8));
-            const float4 a1 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8) + 4);
-            float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            if (HAS_E) {
-                const uint32_t ew[4] = {ecur[q].x, ecur[q].y, ecur[q].z, ecur[q].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t w = ew[e >> 1];
-                    const float xe = __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
-                    v[e] = ep.post * (ep.coef_acc * v[e] + ep.coef_e * xe);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = ep.post * (ep.coef_acc * v[e]);
-            }
-            if (ep.diag != 0.f) {
-                const int64_t dc = brow + rr - (col0 + c8);  // column of the diagonal, relative
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] += (dc == e) ? ep.diag : 0.f;
-            }
-            if constexpr (F32OUT) {
-                // a partial tile of a K-split Gram: fp32, tile-local, no mirror
-                float* o = ep.outF + (int64_t)(band * C::RB + rr) * C::BN + c8;
-                gst(reinterpret_cast<float4*>(o), make_float4(v[0], v[1], v[2], v[3]));
-                gst(reinterpret_cast<float4*>(o + 4), make_float4(v[4], v[5], v[6], v[7]));
-                continue;
-            }
-            uint4 o;
-            o.x = pack2(v[0], v[1]);
-            o.y = pack2(v[2], v[3]);
-            o.z = pack2(v[4], v[5]);
-            o.w = pack2(v[6], v[7]);
-            store_out(ep.out + brow * ep.ld_out + col0, (uint32_t)(rr * ep.ld_out + c8) * 2u, o);
-            if (ep.outT) {
-                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
-                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            }
-        }
-        if (!F32OUT && ep.outT) {
-            epi_barrier<LIGHT>();
-#pragma unroll
-            for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
-                const int ch = q * C::NT + threadIdx.x;
-                const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
-                float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = sb[sbi<C>(i8 + e, c)];
-                uint4 o;
-                o.x = pack2(v[0], v[1]);
-                o.y = pack2(v[2], v[3]);
-                o.z = pack2(v[4], v[5]);
-                o.w = pack2(v[6], v[7]);
-                store_out(ep.outT + col0 * ep.ld_outT + brow, (uint32_t)(c * ep.ld_outT + i8) * 2u, o);
-            }
-        }
-        if (HAS_E) {
-#pragma unroll
-            for (int q = 0; q < QN; ++q) ecur[q] = enxt[q];
-        }
-    }
 }
 
 // Task of this workgroup under an XcdSplit: a whole tile (quarter = -1) or
@@ -834,8 +843,17 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
 // per workgroup spent most of its time in the copy latency and the epilogue,
 // one after the other.  LDS: the two stage arrays (B's slab and X's slab of
 // k 0..63 and of k 64..127) and the epilogue's band buffer.
-template <class C>
-__global__ __launch_bounds__(C::NT) void ns_update_strip_kernel(const MatDesc* __restrict__ descs, int n,
+//
+// NEXT_GRAM: the strip also forms its share of the next iteration's Gram.  A
+// strip covers the same columns as one part of the K-split Gram (the planner
+// makes the strip count per matrix equal the part count), so after each
+// tile's epilogue has left the tile's bf16 values in LDS (in the slabs the
+// X block has vacated), the workgroup multiplies them by themselves into a
+// second accumulator, and stores that as its part's raw fp32 tile at the end:
+// the values and the summation order of the split Gram, without reading X
+// back from memory.
+template <class C, bool NEXT_GRAM>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void ns_update_strip_kernel(const MatDesc* __restrict__ descs, int n,
                                                                 const int32_t* __restrict__ prefix,
                                                                 XcdSplit xs, int it, int strip) {
     static_assert(C::BM == 128 && C::BN == 128 && C::NS == 2 && !C::SPLIT && C::BK == 64,
@@ -850,7 +868,8 @@ __global__ __launch_bounds__(C::NT) void ns_update_strip_kernel(const MatDesc* _
     const MatDesc& d = descs[mi];
     const int64_t mp = d.mp, np = d.np;  // mp == 128
     const int tiles = (int)(np / C::BN);
-    const int j0 = (task - prefix[mi]) * strip;
+    const int part = task - prefix[mi];
+    const int j0 = part * strip;
     const int j1 = min(j0 + strip, tiles);
     const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
     const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
@@ -872,6 +891,18 @@ __global__ __launch_bounds__(C::NT) void ns_update_strip_kernel(const MatDesc* _
     const int frow = lane & 31;
     const int khalf = lane >> 5;
     constexpr int KS = C::BK / 16;
+    // the tile's bf16 values as row slabs, in the X halves of the stage arrays
+    uint16_t* const xo[2] = {stage_q<C>(st, 0), stage_q<C>(st, 1)};
+    const Stages sx{{xo[0], xo[1], xo[1], xo[1]}};
+    f32x16 accg[C::FM][C::FN];
+    if constexpr (NEXT_GRAM) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) accg[i][jj][r] = 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         load_slab<C, C::BM>(B + u * C::BK, mp, stage_p<C>(st, u), wave, lane);
@@ -897,13 +928,53 @@ __global__ __launch_bounds__(C::NT) void ns_update_strip_kernel(const MatDesc* _
             }
         }
         __syncthreads();  // every wave is done with this X block: its slabs may be refilled
-        if (j + 1 < j1) {
+        if constexpr (NEXT_GRAM) {
+            // the tile's bf16 values go to the vacated X slabs, then into the
+            // Gram accumulator; the next X block is copied after that
+            epilogue_bands<C, false, false, true, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow,
+                                                        khalf, xo);
+            lds_barrier();
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np, stage_q<C>(st, u),
-                                wave, lane);
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    Frags<C> f;
+                    read_frags<C, false, true>(sx, u, kk, wm, wn, frow, khalf, lane, f);
+                    mfma_frags<C>(accg, f);
+                }
+            }
+            __syncthreads();  // the tile's slabs are read: the next X block may go there
+            if (j + 1 < j1) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
+                                    stage_q<C>(st, u), wave, lane);
+            }
+        } else {
+            if (j + 1 < j1) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
+                                    stage_q<C>(st, u), wave, lane);
+            }
+            epilogue_bands<C, false, false, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow, khalf);
         }
-        epilogue_bands<C, false, false, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow, khalf);
+    }
+    if constexpr (NEXT_GRAM) {
+        // this strip's part of the next Gram: raw fp32, as the K-split Gram stores it
+        Epi eg;
+        eg.outF = d.gram_part + (int64_t)part * C::BM * C::BN;
+        eg.out = nullptr;
+        eg.ld_out = 0;
+        eg.outT = nullptr;
+        eg.ld_outT = 0;
+        eg.E = nullptr;
+        eg.ld_e = 0;
+        eg.coef_e = 0.f;
+        eg.coef_acc = 1.f;
+        eg.post = 1.f;
+        eg.diag = 0.f;
+        epilogue_bands<C, false, true, true>(accg, 0, 0, eg, band, wm, wn, frow, khalf);
     }
 }
 
@@ -1048,8 +1119,13 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 }
 
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
-                                   const XcdSplit& xs, int it, int strip, hipStream_t st) {
-    ns_update_strip_kernel<SmallCfg><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs, it, strip);
+                                   const XcdSplit& xs, int it, int strip, int next_gram, hipStream_t st) {
+    if (next_gram)
+        ns_update_strip_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs,
+                                                                                      it, strip);
+    else
+        ns_update_strip_kernel<SmallCfg, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip,
+                                                                                       xs, it, strip);
     return hipGetLastError();
 }
 

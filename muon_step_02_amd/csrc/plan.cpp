@@ -414,6 +414,10 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
                 }
                 C.total_strips = C.pstrip[C.count];
                 C.xs_strip = xcd_split(ts.data(), wsz.data(), C.count, cus, 0, 0);
+                bool fuse = C.gram_split;
+                for (int k = 0; k < C.count && fuse; ++k)
+                    fuse = ts[k] == P.d[C.first + k].gram_split;
+                C.fuse_gram = fuse;
             }
         }
     }

@@ -29,6 +29,10 @@ struct ClassPlan {
     size_t off_pstrip = 0;
     int total_strips = 0;
     XcdSplit xs_strip{};
+    // small class, K-split Gram and strips with as many strips per matrix as
+    // Gram parts: from the second iteration on, the update's strips store the
+    // Gram parts and the split Gram launch is skipped
+    bool fuse_gram = false;
     int kmax_n = 0, kmax_m = 0;         // largest padded n' and m' of the class
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };

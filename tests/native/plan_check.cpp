@@ -369,11 +369,15 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
                     EXPECT((int64_t)(C.pstrip[k + 1] - C.pstrip[k] - 1) * C.strip < tiles);
                 }
                 EXPECT(C.total_strips == run);
+                bool fuse = C.gram_split;
+                for (int k = 0; k < C.count; ++k)
+                    fuse = fuse && C.pstrip[k + 1] - C.pstrip[k] == P.d[C.first + k].gram_split;
+                EXPECT(C.fuse_gram == fuse);
                 check_split(C.xs_strip, C.total_strips, cus, 0);
                 EXPECT(memcmp(img.data() + C.off_pstrip, C.pstrip.data(), 4 * (size_t)(C.count + 1)) == 0);
             }
         } else {
-            EXPECT(C.strip == 0);
+            EXPECT(C.strip == 0 && !C.fuse_gram);
         }
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
@@ -510,12 +514,19 @@ int main(int argc, char** argv) {
         // per head: 64 blocks of 128 x 7168 (56 column tiles each) in strips of 7
         plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 7168}), P);
         EXPECT(P.cls[kSmall].strip == 7 && P.cls[kSmall].total_strips == 512);
+        EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram && P.d[0].gram_split == 8);
         // 16 blocks of 100 x 4900 (39 tiles each): strips of 2, the last one short
         plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
         EXPECT(P.cls[kSmall].strip == 2 && P.cls[kSmall].total_strips == 16 * 20);
         // few small tiles: one tile per workgroup
         plan_of({{128, 4096}, {100, 3000}}, P);
-        EXPECT(P.cls[kSmall].strip == 0);
+        EXPECT(P.cls[kSmall].strip == 0 && !P.cls[kSmall].fuse_gram);
+        // 64 heads of 128 x 3584: 7 Gram parts of 8 slabs and 7 strips of 4 tiles
+        plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 3584}), P);
+        EXPECT(P.cls[kSmall].strip == 4 && P.d[0].gram_split == 7 && P.cls[kSmall].fuse_gram);
+        // strips of 2 against 9 Gram parts: no fusion
+        plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
+        EXPECT(P.cls[kSmall].gram_split && !P.cls[kSmall].fuse_gram);
     }
     // xcd_split on its own: degenerate inputs
     {

@@ -245,3 +245,34 @@ def test_small_class_update_in_strips():
         assert relF(f64(M[i]), Mr) <= TOL_STATE, i
         assert relF(f64(W[i]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(*W0.shape), Or, Wr,
                                                   TOL_O_BF16), i
+
+
+def test_per_head_gram_parts_from_update_strips():
+    # 64 heads of 128 x 3584 (rows of one 8192 x 3584 tensor): the small class
+    # takes a K-split Gram of 7 parts and an update in 7 strips of 4 column
+    # tiles per head, the same column ranges, so from the second iteration on
+    # the update's strips store the Gram parts and no split Gram launch runs.
+    # Sampled heads against the oracle over two steps (momentum carried).
+    heads, dh, dm = 64, 128, 3584
+    Wf = _weight(heads * dh, dm, 7)
+    Mf = torch.zeros(heads * dh, dm, device=DEV)
+    Of = torch.empty(heads * dh, dm, device=DEV)
+    sample = [0, 1, 9, 31, 32, 47, 62, 63]
+    ref = {h: [f64(Wf[h * dh:(h + 1) * dh]), np.zeros((dh, dm))] for h in sample}
+    kw = oracle_kwargs(BASE_HP)
+    for step in range(2):
+        Gf = _grad(heads * dh, dm, 200 + step)
+        mats = [mu.muon_matrix(Wf[h * dh:(h + 1) * dh], Gf[h * dh:(h + 1) * dh], Mf[h * dh:(h + 1) * dh],
+                               update_out=Of[h * dh:(h + 1) * dh]) for h in range(heads)]
+        run_muon_step(mats, hp_from(BASE_HP))
+        torch.cuda.synchronize()
+        for h in sample:
+            sl = slice(h * dh, (h + 1) * dh)
+            W0, M0 = ref[h]
+            Wr, Mr, Or = oracle.muon_matrix_step(W0, f64(Gf[sl]), M0, **kw)
+            assert relF(f64(Of[sl]), Or) <= TOL_O_BF16, (step, h)
+            assert relF(f64(Mf[sl]), Mr) <= TOL_STATE, (step, h)
+            assert relF(f64(Wf[sl]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(dh, dm), Or, Wr,
+                                                       TOL_O_BF16), (step, h)
+            # carry the GPU's own state, so each step is checked on its own
+            ref[h] = [f64(Wf[sl]), f64(Mf[sl])]
