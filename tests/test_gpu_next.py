@@ -247,24 +247,29 @@ def test_small_class_update_in_strips():
                                                   TOL_O_BF16), i
 
 
-def test_per_head_gram_parts_from_update_strips():
+@pytest.mark.parametrize("hpd", [BASE_HP, dict(BASE_HP, steps=2),
+                                 dict(BASE_HP, steps=3, coeffs=[3.4445, -4.7750, 2.0315,
+                                                                3.0, -3.2, 1.2, 1.875, -1.25, 0.375])],
+                         ids=["5 steps", "2 steps", "3 steps, schedule"])
+def test_per_head_gram_parts_from_update_strips(hpd):
     # 64 heads of 128 x 3584 (rows of one 8192 x 3584 tensor): the small class
     # takes a K-split Gram of 7 parts and an update in 7 strips of 4 column
     # tiles per head, the same column ranges, so from the second iteration on
     # the update's strips store the Gram parts and no split Gram launch runs.
-    # Sampled heads against the oracle over two steps (momentum carried).
+    # Sampled heads against the oracle over two steps (momentum carried), for
+    # an odd and an even iteration count and a coefficient schedule.
     heads, dh, dm = 64, 128, 3584
     Wf = _weight(heads * dh, dm, 7)
     Mf = torch.zeros(heads * dh, dm, device=DEV)
     Of = torch.empty(heads * dh, dm, device=DEV)
     sample = [0, 1, 9, 31, 32, 47, 62, 63]
     ref = {h: [f64(Wf[h * dh:(h + 1) * dh]), np.zeros((dh, dm))] for h in sample}
-    kw = oracle_kwargs(BASE_HP)
+    kw = oracle_kwargs(hpd)
     for step in range(2):
         Gf = _grad(heads * dh, dm, 200 + step)
         mats = [mu.muon_matrix(Wf[h * dh:(h + 1) * dh], Gf[h * dh:(h + 1) * dh], Mf[h * dh:(h + 1) * dh],
                                update_out=Of[h * dh:(h + 1) * dh]) for h in range(heads)]
-        run_muon_step(mats, hp_from(BASE_HP))
+        run_muon_step(mats, hp_from(hpd))
         torch.cuda.synchronize()
         for h in sample:
             sl = slice(h * dh, (h + 1) * dh)
