@@ -46,6 +46,8 @@ namespace muon {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -834,6 +836,78 @@ __global__ __launch_bounds__(C::NT) void ns_update_kernel(const MatDesc* __restr
     }
 }
 
+// The products with the operand roles exchanged: acc[i][j] += Q-block j times
+// P-block i, i.e. the transpose of the P Q' block.  Lane l, register r then
+// holds row (l & 31) of the P block and column 8 (r >> 2) + 4 (l >> 5) +
+// (r & 3) of the Q block: four consecutive columns of one row per group of
+// four registers, which the strip epilogue stores without a pass through LDS.
+template <class C>
+__device__ __forceinline__ void mfma_frags_rows(f32x16 (&acc)[C::FM][C::FN], const Frags<C>& f) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// Strip epilogue, first half: the tile held in rows (mfma_frags_rows) is
+// scaled, rounded to bf16 and written to LDS as two row slabs of 64 columns
+// (xo[0], xo[1]; load_slab's layout), four columns (8 bytes) per write.
+template <class C>
+__device__ __forceinline__ void rows_to_slabs(const f32x16 (&acc)[C::FM][C::FN], const Epi& ep,
+                                              int wm, int wn, int frow, int khalf,
+                                              uint16_t* const* xo) {
+    static_assert(C::BN == 128 && C::BK == 64 && C::TN == 64, "a wave's columns are one 64-column slab");
+    // the wave's slab (a select, not an index, so the LDS address space is kept)
+    uint16_t* const xs = wn == 0 ? xo[0] : xo[1];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int row = wm * C::TM + i * 32 + frow;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int lch = 4 * j + g;  // chunk of columns j * 32 + 8 g .. + 7 within the slab
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = ep.post * (ep.coef_acc * acc[i][j][4 * g + e]);
+                const bf16x4 h = __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4);
+                *reinterpret_cast<uint2*>(xs + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3) + 4 * khalf) =
+                    __builtin_bit_cast(uint2, h);
+            }
+        }
+    }
+}
+
+// Second half: every thread reads 8 chunks of 16 bytes from the slabs, so
+// that one wave's store covers 8 rows x 64 columns: eight whole 128-byte
+// lines.  Chunk q of thread t: row 32 (q >> 1) + t / 8, slab q & 1, logical
+// chunk t % 8 (16 lanes read two rows of one slab: all 64 banks once).
+template <class C>
+struct SlabRows {
+    uint4 v[8];
+};
+template <class C>
+__device__ __forceinline__ void read_slab_rows(uint16_t* const* xo, SlabRows<C>& r) {
+    static_assert(C::NT == 256 && C::BM == 128, "8 chunks per thread cover the 128 x 128 tile");
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 32 * (q >> 1) + (t >> 3), lch = t & 7;
+        const uint16_t* xs = (q & 1) ? xo[1] : xo[0];
+        r.v[q] = *reinterpret_cast<const uint4*>(xs + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3));
+    }
+}
+template <class C>
+__device__ __forceinline__ void store_slab_rows(const SlabRows<C>& r, int64_t col0, const Epi& ep) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 32 * (q >> 1) + (t >> 3), c = 64 * (q & 1) + 8 * (t & 7);
+        store_out(ep.out + col0, (uint32_t)(row * ep.ld_out + c) * 2u, r.v[q]);
+    }
+}
+
 // Update of the small class in strips.  Its matrices have m' = 128, so B is
 // one 128 x 128 tile and an update tile is B times one 128-column block of X
 // (K = 128: two slabs).  A workgroup takes `strip` consecutive column tiles
@@ -924,16 +998,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             for (int kk = 0; kk < KS; ++kk) {
                 Frags<C> f;
                 read_frags<C, true>(st, u, kk, wm, wn, frow, khalf, lane, f);
-                mfma_frags<C>(acc, f);
+                mfma_frags_rows<C>(acc, f);
             }
         }
-        __syncthreads();  // every wave is done with this X block: its slabs may be refilled
+        // the tile's bf16 values go to the X slabs this block has vacated;
+        // from there they are stored (and, for NEXT_GRAM, multiplied into the
+        // Gram accumulator) before the next X block is copied in
+        lds_barrier();  // every wave is done with this X block
+        rows_to_slabs<C>(acc, ep, wm, wn, frow, khalf, xo);
+        lds_barrier();
+        SlabRows<C> out;
+        read_slab_rows<C>(xo, out);
         if constexpr (NEXT_GRAM) {
-            // the tile's bf16 values go to the vacated X slabs, then into the
-            // Gram accumulator; the next X block is copied after that
-            epilogue_bands<C, false, false, true, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow,
-                                                        khalf, xo);
-            lds_barrier();
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -943,22 +1019,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                     mfma_frags<C>(accg, f);
                 }
             }
-            __syncthreads();  // the tile's slabs are read: the next X block may go there
-            if (j + 1 < j1) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
-                                    stage_q<C>(st, u), wave, lane);
-            }
-        } else {
-            if (j + 1 < j1) {
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-                    load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
-                                    stage_q<C>(st, u), wave, lane);
-            }
-            epilogue_bands<C, false, false, true>(acc, 0, (int64_t)j * C::BN, ep, band, wm, wn, frow, khalf);
         }
+        lds_barrier();  // the tile's slabs are read: the next X block may go there
+        if (j + 1 < j1) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
+                                stage_q<C>(st, u), wave, lane);
+        }
+        store_slab_rows<C>(out, (int64_t)j * C::BN, ep);
     }
     if constexpr (NEXT_GRAM) {
         // this strip's part of the next Gram: raw fp32, as the K-split Gram stores it
