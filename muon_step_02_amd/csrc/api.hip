@@ -290,7 +290,8 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
         }
         for (int k = 0; k < kNumClasses && e == hipSuccess; ++k) {
             const ClassPlan& C = P.cls[k];
-            if (C.count == 0) continue;
+            // a class updated in strips forms B inside the strips
+            if (C.count == 0 || C.strip > 0) continue;
             const MatDesc* dc = dd + C.first;
             const hipStream_t sk = cs[k];
             Prefix pp = pc[k];  // the polynomial's own tiling (128-tiles when poly_small)
@@ -312,7 +313,7 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                     return launch_update_strip_bf16(dc, C.count,
                                                     reinterpret_cast<const int32_t*>(ws + C.off_pstrip),
                                                     C.xs_strip, it, C.strip,
-                                                    C.fuse_gram && it + 1 < hp->ns_steps, sk);
+                                                    C.fuse_gram && it + 1 < hp->ns_steps, a, b, c, sk);
                 return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }

@@ -908,34 +908,42 @@ __device__ __forceinline__ void store_slab_rows(const SlabRows<C>& r, int64_t co
     }
 }
 
-// Update of the small class in strips.  Its matrices have m' = 128, so B is
-// one 128 x 128 tile and an update tile is B times one 128-column block of X
-// (K = 128: two slabs).  A workgroup takes `strip` consecutive column tiles
-// of one matrix: B's two slabs are copied to LDS once, and the X block of the
-// next tile is copied while the current tile's epilogue runs (its band
-// barriers carry no memory fence, so those copies stay in flight).  One tile
-// per workgroup spent most of its time in the copy latency and the epilogue,
-// one after the other.  LDS: the two stage arrays (B's slab and X's slab of
-// k 0..63 and of k 64..127) and the epilogue's band buffer.
+// Update of the small class in strips.  Its matrices have m' = 128, so A and
+// B are one 128 x 128 tile each and an update tile is B times one 128-column
+// block of X (K = 128: two slabs).  A workgroup takes `strip` consecutive
+// column tiles of one matrix.  It first forms B = a I + b A + c A A itself
+// from A (the polynomial, 4 MFLOP, once per strip instead of a launch of its
+// own), in LDS, then runs its tiles; the X block of the next tile is copied
+// while the current tile's epilogue runs.  One tile per workgroup spent most
+// of its time in the copy latency and the epilogue, one after the other.
+//
+// The products are held in rows (mfma_frags_rows), so the epilogue writes
+// each tile once to LDS as bf16, in the X slabs the block has vacated, and
+// stores it from there as whole 128-byte lines.
 //
 // NEXT_GRAM: the strip also forms its share of the next iteration's Gram.  A
 // strip covers the same columns as one part of the K-split Gram (the planner
-// makes the strip count per matrix equal the part count), so after each
-// tile's epilogue has left the tile's bf16 values in LDS (in the slabs the
-// X block has vacated), the workgroup multiplies them by themselves into a
+// makes the strip count per matrix equal the part count), so once a tile's
+// bf16 values sit in LDS the workgroup multiplies them by themselves into a
 // second accumulator, and stores that as its part's raw fp32 tile at the end:
 // the values and the summation order of the split Gram, without reading X
 // back from memory.
+//
+// LDS, in variables of their own so that the compiler can tell the copies
+// into one from the accesses to another: A's (then B's) two slabs (32 KB),
+// the X block's two k-major slabs (k 0..63, 64..127; later the tile's two
+// 64-column row slabs; 16 KB each) and the fp32 band buffer of the final
+// Gram store (16 KB).
 template <class C, bool NEXT_GRAM>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void ns_update_strip_kernel(const MatDesc* __restrict__ descs, int n,
-                                                                const int32_t* __restrict__ prefix,
-                                                                XcdSplit xs, int it, int strip) {
-    static_assert(C::BM == 128 && C::BN == 128 && C::NS == 2 && !C::SPLIT && C::BK == 64,
-                  "two stage arrays hold the whole K of 128");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds0[kLdsArr];
-    __shared__ __attribute__((aligned(1024))) uint16_t lds1[kLdsArr];
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void ns_update_strip_kernel(
+    const MatDesc* __restrict__ descs, int n, const int32_t* __restrict__ prefix, XcdSplit xs, int it,
+    int strip, float ca, float cb, float cc) {
+    static_assert(C::BM == 128 && C::BN == 128 && C::BK == 64 && C::NT == 256,
+                  "two 64-deep slabs hold the whole K of 128");
+    __shared__ __attribute__((aligned(1024))) uint16_t lp[2 * C::BM * C::BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t lx0[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t lx1[C::BK * C::BN];
     __shared__ __attribute__((aligned(1024))) float band[C::RB * C::BN];
-    const Stages st{{lds0, lds1, lds1, lds1}};
     int task, q;
     if (!xcd_task(xs, task, q)) return;  // no quarter tasks
     const int mi = find_matrix(prefix, n, task);
@@ -945,7 +953,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int part = task - prefix[mi];
     const int j0 = part * strip;
     const int j1 = min(j0 + strip, tiles);
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(d.b);
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(d.a);
     const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
     Epi ep;
     ep.outF = nullptr;
@@ -965,42 +973,126 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int frow = lane & 31;
     const int khalf = lane >> 5;
     constexpr int KS = C::BK / 16;
-    // the tile's bf16 values as row slabs, in the X halves of the stage arrays
-    uint16_t* const xo[2] = {stage_q<C>(st, 0), stage_q<C>(st, 1)};
-    const Stages sx{{xo[0], xo[1], xo[1], xo[1]}};
+    uint16_t* const xo[2] = {lx0, lx1};
+    uint16_t* const lp0 = lp;
+    uint16_t* const lp1 = lp + C::BM * C::BK;
+    // fragments of k-step kk of slab u: rows of the (A or B) slab against rows
+    // of the same slab (RR), or against the k-major X block (else)
+    auto frags = [&](int u, int kk, bool xkn, bool xrows, Frags<C>& f) {
+        const uint16_t* sp = xrows ? (u ? lx1 : lx0) : (u ? lp1 : lp0);
+        const uint16_t* sq = (xkn || xrows) ? (u ? lx1 : lx0) : sp;
+        const int lch = 2 * kk + khalf;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
+#pragma unroll
+        for (int jj = 0; jj < C::FN; ++jj)
+            f.b[jj] = xkn ? read_frag_kn<C>(sq, 16 * kk, wn * C::TN + jj * 32, lane)
+                          : read_frag<C>(sq, wn * C::TN + jj * 32 + frow, lch);
+    };
+    f32x16 acc[C::FM][C::FN];
     f32x16 accg[C::FM][C::FN];
-    if constexpr (NEXT_GRAM) {
+    auto zero = [](f32x16(&t)[C::FM][C::FN]) {
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int jj = 0; jj < C::FN; ++jj)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) accg[i][jj][r] = 0.f;
-    }
+                for (int r = 0; r < 16; ++r) t[i][jj][r] = 0.f;
+    };
+    if constexpr (NEXT_GRAM) zero(accg);
+
+    // A's slabs, then the first X block; A is waited for alone
+    load_slab<C, C::BM>(A, mp, lp0, wave, lane);
+    load_slab<C, C::BM>(A + C::BK, mp, lp1, wave, lane);
+    load_slab_kn<C>(X + (int64_t)j0 * C::BN, np, lx0, wave, lane);
+    load_slab_kn<C>(X + (int64_t)C::BK * np + (int64_t)j0 * C::BN, np, lx1, wave, lane);
+    constexpr int LX = 2 * ((C::BK / (64 / (C::BN / 8))) / C::NW);  // this wave's X copies
+    wait_vmcnt<LX>();
+    lds_barrier();
+    // B = a I + b A + c A A (the polynomial's epilogue arithmetic), written
+    // over A in place once every wave has read A
+    {
+        zero(acc);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        load_slab<C, C::BM>(B + u * C::BK, mp, stage_p<C>(st, u), wave, lane);
-        load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)j0 * C::BN, np, stage_q<C>(st, u), wave, lane);
-    }
-    for (int j = j0; j < j1; ++j) {
-        wait_vmcnt<0>();  // B and this tile's X have landed (and the last tile's stores)
-        __syncthreads();
-        f32x16 acc[C::FM][C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < C::FN; ++jj)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
                 Frags<C> f;
-                read_frags<C, true>(st, u, kk, wm, wn, frow, khalf, lane, f);
+                frags(u, kk, false, false, f);
                 mfma_frags_rows<C>(acc, f);
             }
-        }
+        // The wave's columns wn*64 .. +63 of A are slab wn; a lane's four
+        // columns are half khalf of chunk 4 jj + g of its row.  LDS is read
+        // and written in whole 16-byte chunks: lanes l and l + 32 trade halves
+        // (chunk g of a pair goes through lane l, chunk g + 1 through lane
+        // l + 32).  Paired 8-byte accesses would be merged into one
+        // instruction, which the compiler's copy tracking cannot tell apart
+        // from the X copies in flight; it would wait for those.
+        auto trade = [](uint2 v) {
+            return make_uint2((uint32_t)__shfl_xor((int)v.x, 32, 64), (uint32_t)__shfl_xor((int)v.y, 32, 64));
+        };
+        auto poly_epilogue = [&](uint16_t* ps) {
+            uint2 e[C::FM][C::FN][4];
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < C::FN; ++jj)
+#pragma unroll
+                    for (int gp = 0; gp < 4; gp += 2) {
+                        const int row = wm * C::TM + i * 32 + frow;
+                        const int ck = 4 * jj + gp + khalf;
+                        const uint4 r = *reinterpret_cast<const uint4*>(ps + row * C::BK + ((ck ^ swz<C::BK>(row)) << 3));
+                        const uint2 lo = make_uint2(r.x, r.y), hi = make_uint2(r.z, r.w);
+                        const uint2 got = trade(khalf ? lo : hi);
+                        e[i][jj][gp] = khalf ? got : lo;
+                        e[i][jj][gp + 1] = khalf ? hi : got;
+                    }
+            lds_barrier();  // every wave has read A
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int jj = 0; jj < C::FN; ++jj) {
+                    const int row = wm * C::TM + i * 32 + frow;
+                    uint2 o[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = wn * C::TN + jj * 32 + 8 * g + 4 * khalf;
+                        const uint32_t w[2] = {e[i][jj][g].x, e[i][jj][g].y};
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const uint32_t h = w[t >> 1];
+                            const float av = __builtin_bit_cast(float, (t & 1) ? (h & 0xffff0000u) : (h << 16));
+                            v[t] = 1.f * (cc * acc[i][jj][4 * g + t] + cb * av);
+                            if (row == col + t) v[t] += ca;
+                        }
+                        o[g] = __builtin_bit_cast(uint2, __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4));
+                    }
+#pragma unroll
+                    for (int gp = 0; gp < 4; gp += 2) {
+                        const int ck = 4 * jj + gp + khalf;
+                        const uint2 got = trade(khalf ? o[gp] : o[gp + 1]);
+                        const uint4 wv = khalf ? make_uint4(got.x, got.y, o[gp + 1].x, o[gp + 1].y)
+                                               : make_uint4(o[gp].x, o[gp].y, got.x, got.y);
+                        *reinterpret_cast<uint4*>(ps + row * C::BK + ((ck ^ swz<C::BK>(row)) << 3)) = wv;
+                    }
+                }
+        };
+        poly_epilogue(lp + wn * (C::BM * C::BK));
+    }
+
+    for (int j = j0; j < j1; ++j) {
+        wait_vmcnt<0>();  // this tile's X has landed (and the last tile's stores)
+        __syncthreads();  // ... in every wave; B is written
+        zero(acc);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                Frags<C> f;
+                frags(u, kk, true, false, f);
+                mfma_frags_rows<C>(acc, f);
+            }
         // the tile's bf16 values go to the X slabs this block has vacated;
         // from there they are stored (and, for NEXT_GRAM, multiplied into the
         // Gram accumulator) before the next X block is copied in
@@ -1011,21 +1103,18 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         read_slab_rows<C>(xo, out);
         if constexpr (NEXT_GRAM) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int kk = 0; kk < KS; ++kk) {
                     Frags<C> f;
-                    read_frags<C, false, true>(sx, u, kk, wm, wn, frow, khalf, lane, f);
+                    frags(u, kk, false, true, f);
                     mfma_frags<C>(accg, f);
                 }
-            }
         }
         lds_barrier();  // the tile's slabs are read: the next X block may go there
         if (j + 1 < j1) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                load_slab_kn<C>(X + (int64_t)u * C::BK * np + (int64_t)(j + 1) * C::BN, np,
-                                stage_q<C>(st, u), wave, lane);
+            load_slab_kn<C>(X + (int64_t)(j + 1) * C::BN, np, lx0, wave, lane);
+            load_slab_kn<C>(X + (int64_t)C::BK * np + (int64_t)(j + 1) * C::BN, np, lx1, wave, lane);
         }
         store_slab_rows<C>(out, (int64_t)j * C::BN, ep);
     }
@@ -1188,13 +1277,14 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 }
 
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
-                                   const XcdSplit& xs, int it, int strip, int next_gram, hipStream_t st) {
+                                   const XcdSplit& xs, int it, int strip, int next_gram, float a, float b,
+                                   float c, hipStream_t st) {
     if (next_gram)
         ns_update_strip_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs,
-                                                                                      it, strip);
+                                                                                      it, strip, a, b, c);
     else
-        ns_update_strip_kernel<SmallCfg, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip,
-                                                                                       xs, it, strip);
+        ns_update_strip_kernel<SmallCfg, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
+            d, n, prefix_strip, xs, it, strip, a, b, c);
     return hipGetLastError();
 }
 

@@ -95,11 +95,13 @@ hipError_t launch_poly_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& x
 hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit& xs, int it,
                               int small, hipStream_t st);
 // the small class's update in strips of `strip` consecutive column tiles per
-// workgroup; prefix_strip: strips per matrix, prefix-summed.  next_gram: each
-// strip also stores its part of the next iteration's K-split Gram (the
-// strip count per matrix equals its gram_split)
+// workgroup; prefix_strip: strips per matrix, prefix-summed.  Each strip
+// forms B = a I + b A + c A A from A itself (no polynomial launch for the
+// class).  next_gram: each strip also stores its part of the next
+// iteration's K-split Gram (the strip count per matrix equals its gram_split)
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
-                                   const XcdSplit& xs, int it, int strip, int next_gram, hipStream_t st);
+                                   const XcdSplit& xs, int it, int strip, int next_gram, float a, float b,
+                                   float c, hipStream_t st);
 
 // fp32 class (every tile of the symmetric products; p.gram == p.tri).
 // kmax: the largest K of the launch's matrices (n' for the Gram, m' for the
