@@ -1136,6 +1136,259 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
 }
 
+// ---- fp32 operands: the full-precision option on the matrix cores ---------
+//
+// The fp32 class's three products (X and X^T kept side by side, 64-padded;
+// the arithmetic of the FMA kernels in gemm_f32.hip, but the symmetric
+// outputs computed on the lower triangle of tiles and mirrored) on the slab
+// machinery above: a slab row of 128 bytes holds 32
+// fp32 values where it holds 64 bf16, so the copies, the swizzle and the
+// fragment reads serve unchanged, with K and the leading dimensions counted
+// in 2-byte units.  A 16-byte fragment then holds 4 fp32 k values, and feeds
+// four v_mfma_f32_32x32x2f32: in MFMA t, the lanes of k-half h contribute k =
+// 8 kk + 4 h + t, so the four sum k-step kk's 8 values.
+//
+// 64 x 64 tiles (the fp32 padding), four waves of one 32 x 32 block each,
+// two 16 KB stages (several workgroups per compute unit); 1 B copied per 16
+// flop.
+
+template <class C>
+__device__ __forceinline__ void mfma_frags_f32(f32x16 (&acc)[C::FM][C::FN], const Frags<C>& f) {
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            const f32x4 a = __builtin_bit_cast(f32x4, f.a[i]);
+            const f32x4 b = __builtin_bit_cast(f32x4, f.b[j]);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc[i][j], 0, 0, 0);
+        }
+}
+
+// C tile = sum_k P[i][k] Q[j][k] over fp32 rows (K fp32 values, a multiple of
+// 32), the pipeline of gemm_tile with the fp32 products.  Its barriers are
+// LDS-only: each wave has waited for its own copies of the stage it reads
+// next.
+template <class C>
+__device__ __forceinline__ void gemm_mainloop_f32(const float* __restrict__ P, int64_t ldp,
+                                                  const float* __restrict__ Q, int64_t ldq, int K,
+                                                  const Stages& st, f32x16 (&acc)[C::FM][C::FN]) {
+    const uint16_t* P0 = reinterpret_cast<const uint16_t*>(P);
+    const uint16_t* Q0 = reinterpret_cast<const uint16_t*>(Q);
+    ldp *= 2;
+    ldq *= 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int KT = (2 * K) / C::BK;
+    constexpr int KS = C::BK / 16;
+#pragma unroll
+    for (int u = 0; u < C::NS; ++u)
+        if (u < KT) load_stage<C, false>(P0, ldp, Q0, ldq, (int64_t)u * C::BK, st, u, wave, lane);
+    if (KT >= C::NS) wait_vmcnt<(C::NS - 1) * C::LPS>(); else wait_vmcnt<0>();
+    lds_barrier();
+    Frags<C> f[2];
+    read_frags<C, false>(st, 0, 0, wm, wn, frow, khalf, lane, f[0]);
+    for (int kt0 = 0; kt0 < KT; kt0 += C::NS) {
+#pragma unroll
+        for (int u = 0; u < C::NS; ++u) {
+            const int kt = kt0 + u;
+            if (kt < KT) {
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) {
+                    if (kk + 1 < KS) {
+                        read_frags<C, false>(st, u, kk + 1, wm, wn, frow, khalf, lane, f[(kk + 1) & 1]);
+                    } else {
+                        if (kt + C::NS - 1 < KT) wait_vmcnt<(C::NS - 2) * C::LPS>(); else wait_vmcnt<0>();
+                        lds_barrier();
+                        if (kt + C::NS < KT)
+                            load_stage<C, false>(P0, ldp, Q0, ldq, (int64_t)(kt + C::NS) * C::BK, st, u, wave,
+                                                 lane);
+                        read_frags<C, false>(st, (u + 1) % C::NS, 0, wm, wn, frow, khalf, lane, f[0]);
+                    }
+                    mfma_frags_f32<C>(acc, f[kk & 1]);
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();
+}
+
+// Epilogue of an fp32 tile through the band buffer (array 0): v = post *
+// (coef_acc * product + coef_e * E), stored to `out` and, if set, transposed
+// to `outT`; every access 2 x 16 bytes.
+struct EpiF32 {
+    float* out;
+    int64_t ld_out;
+    float* outT;
+    int64_t ld_outT;
+    const float* E;
+    int64_t ld_e;
+    float coef_e, coef_acc, post;
+};
+
+template <class C>
+__device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[C::FM][C::FN], int64_t row0, int64_t col0,
+                                             const EpiF32& ep, float* sb) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
+#pragma unroll
+    for (int band = 0; band < C::BM / C::RB; ++band) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+            if (wm * C::TM + i * 32 == band * C::RB) {
+#pragma unroll
+                for (int j = 0; j < C::FN; ++j) {
+                    const int c = wn * C::TN + j * 32 + frow;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sb[sbi<C>(8 * (r >> 2) + 4 * khalf + (r & 3), c)] = acc[i][j][r];
+                }
+            }
+        }
+        __syncthreads();
+        const int64_t brow = row0 + (int64_t)band * C::RB;
+#pragma unroll
+        for (int q = 0; q < (C::RB * C::BN / 8) / C::NT; ++q) {
+            const int ch = q * C::NT + threadIdx.x;
+            const int rr = ch / (C::BN / 8), c8 = (ch % (C::BN / 8)) * 8;
+            const float4 a0 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8));
+            const float4 a1 = *reinterpret_cast<const float4*>(sb + sbi<C>(rr, c8) + 4);
+            float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            if (ep.E) {
+                const float* e = ep.E + (brow + rr) * ep.ld_e + col0 + c8;
+                const float4 e0 = gld(reinterpret_cast<const float4*>(e));
+                const float4 e1 = gld(reinterpret_cast<const float4*>(e + 4));
+                const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = ep.post * (ep.coef_acc * v[t] + ep.coef_e * ev[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = ep.post * (ep.coef_acc * v[t]);
+            }
+            float* o = ep.out + (brow + rr) * ep.ld_out + col0 + c8;
+            gst(reinterpret_cast<float4*>(o), make_float4(v[0], v[1], v[2], v[3]));
+            gst(reinterpret_cast<float4*>(o + 4), make_float4(v[4], v[5], v[6], v[7]));
+            if (ep.outT) {
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            }
+        }
+        if (ep.outT) {
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < (C::BN * C::RB / 8) / C::NT; ++q) {
+                const int ch = q * C::NT + threadIdx.x;
+                const int c = ch / (C::RB / 8), i8 = (ch % (C::RB / 8)) * 8;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sb[sbi<C>(i8 + e, c)];
+                float* o = ep.outT + (col0 + c) * ep.ld_outT + brow + i8;
+                gst(reinterpret_cast<float4*>(o), make_float4(v[0], v[1], v[2], v[3]));
+                gst(reinterpret_cast<float4*>(o + 4), make_float4(v[4], v[5], v[6], v[7]));
+            }
+        }
+    }
+}
+
+using F32Cfg = Cfg<64, 64, 2, 2, 64, 2>;
+
+// One fp32 tile per workgroup, over the class's prefix of (full-square or
+// update) tiles.
+template <int PHASE>
+__global__ __launch_bounds__(F32Cfg::NT) void ns_f32_mfma_kernel(const MatDesc* __restrict__ descs, int n,
+                                                                 const int32_t* __restrict__ prefix, int it,
+                                                                 float ca, float cb, float cc) {
+    using C = F32Cfg;
+    static_assert(C::BM == kTileF32 && C::BN == kTileF32, "fp32 tiles");
+    static_assert(C::NS == 2, "two stages");
+    __shared__ __attribute__((aligned(1024))) uint16_t l0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t l1[C::STAGE];
+    const Stages st{{l0, l1, l1, l1}};
+    const int tile = blockIdx.x;
+    const int mi = find_matrix(prefix, n, tile);
+    const MatDesc& d = descs[mi];
+    const int lt = tile - prefix[mi];
+    const int64_t mp = d.mp, np = d.np;
+    int ti, tj;
+    if (PHASE == UPDATE) {
+        const int tcols = (int)(np / C::BN);
+        ti = lt / tcols;
+        tj = lt - ti * tcols;
+    } else {
+        // the symmetric products: the class's prefix counts every tile of
+        // the square; the first T (T + 1) / 2 of a matrix take the lower
+        // triangle (each off-diagonal tile also stored mirrored), the rest
+        // have nothing to do
+        const int T = (int)(mp / C::BM);
+        if (lt >= T * (T + 1) / 2) return;
+        tri_index(lt, ti, tj);
+    }
+    const float *P, *Q;
+    int64_t ld;
+    int K;
+    EpiF32 ep;
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
+    ep.coef_acc = 1.f;
+    ep.post = 1.f;
+    if (PHASE == GRAM) {
+        P = Q = reinterpret_cast<const float*>(d.x[it & 1]);
+        ld = np;
+        K = (int)np;
+        const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
+        ep.coef_acc = s * s;
+        ep.out = reinterpret_cast<float*>(d.a);
+        ep.ld_out = mp;
+        ep.outT = ti == tj ? nullptr : ep.out;
+        ep.ld_outT = mp;
+    } else if (PHASE == POLY) {
+        P = Q = reinterpret_cast<const float*>(d.a);
+        ld = mp;
+        K = (int)mp;
+        ep.E = P;
+        ep.ld_e = mp;
+        ep.coef_e = cb;
+        ep.coef_acc = cc;
+        ep.out = reinterpret_cast<float*>(d.b);
+        ep.ld_out = mp;
+        ep.outT = ti == tj ? nullptr : ep.out;
+        ep.ld_outT = mp;
+    } else {
+        P = reinterpret_cast<const float*>(d.b);
+        Q = reinterpret_cast<const float*>(d.xt[it & 1]);
+        ld = mp;
+        K = (int)mp;
+        ep.E = reinterpret_cast<const float*>(d.x[it & 1]);
+        ep.ld_e = np;
+        ep.coef_e = ca;
+        ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
+        ep.out = reinterpret_cast<float*>(d.x[(it + 1) & 1]);
+        ep.ld_out = np;
+        ep.outT = reinterpret_cast<float*>(d.xt[(it + 1) & 1]);
+        ep.ld_outT = mp;
+    }
+    const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
+    f32x16 acc[C::FM][C::FN];
+    gemm_mainloop_f32<C>(P + r0 * ld, ld, Q + c0 * ld, ld, K, st, acc);
+    epilogue_f32<C>(acc, r0, c0, ep, reinterpret_cast<float*>(lds_arr(st, 0)));
+}
+
 // single-matrix variants for the test hooks
 template <class C, int PHASE>
 __global__ __launch_bounds__(C::NT) void ns_sym_single(const uint16_t* __restrict__ src, int64_t ld,
@@ -1321,6 +1574,17 @@ hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int
     ns_update_single<UpdCfg><<<xcd_grid(xs), UpdCfg::NT, 0, st>>>(
         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
         reinterpret_cast<uint16_t*>(Xo), m, n, ldx, ldb, s, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_f32_mfma(int phase, const MatDesc* d, int n, const int32_t* prefix, int total, int it,
+                           float a, float b, float c, hipStream_t st) {
+    if (phase == GRAM)
+        ns_f32_mfma_kernel<GRAM><<<total, F32Cfg::NT, 0, st>>>(d, n, prefix, it, a, b, c);
+    else if (phase == POLY)
+        ns_f32_mfma_kernel<POLY><<<total, F32Cfg::NT, 0, st>>>(d, n, prefix, it, a, b, c);
+    else
+        ns_f32_mfma_kernel<UPDATE><<<total, F32Cfg::NT, 0, st>>>(d, n, prefix, it, a, b, c);
     return hipGetLastError();
 }
 

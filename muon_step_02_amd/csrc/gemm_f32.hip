@@ -228,7 +228,7 @@ hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total,
     else if (kmax <= 256)
         ns_f32_shortk_kernel<PHASE, 256><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
     else
-        ns_f32_kernel<PHASE><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+        return launch_f32_mfma(PHASE, d, n, prefix, total, it, a, b, c, st);
     return hipGetLastError();
 }
 
