@@ -1,12 +1,12 @@
 // fp32 Newton-Schulz phases (the full-precision option of the Muon step).
 //
 // Same three products and the same buffer layout as the bf16 kernels (X and
-// X^T kept side by side, padded to multiples of 64, zero padding), computed
-// with fp32 FMAs on 64 x 64 tiles: 256 threads, 4 x 4 outputs each, K in
-// slabs of 16 staged through LDS, or, when every matrix of a launch has K of
-// at most 256, the whole K extent staged at once.  This path serves small
-// matrices where accuracy matters more than throughput, so every tile of the
-// symmetric outputs is computed (no triangle skipping).
+// X^T kept side by side, padded to multiples of 64, zero padding).  A launch
+// whose K exceeds 64 runs on the matrix cores (launch_f32_mfma, with the bf16
+// kernels' slab machinery).  A launch of tiny matrices only (K at most 64,
+// e.g. thousands of at most 32 x 32 blocks) runs here, with fp32 FMAs on
+// 64 x 64 tiles: 256 threads, 4 x 4 outputs each, the tile's whole K extent
+// staged in LDS at once, every tile of the symmetric outputs computed.
 //
 //   gram:   A = s^2 X X^T        (s = 1/(||Y||+eps) on the first iteration)
 //   poly:   B = b A + c A A
@@ -115,54 +115,10 @@ __device__ __forceinline__ void f32_epilogue(const F32Tile<PHASE>& t, const floa
     }
 }
 
-// K in slabs of KS through LDS (any K, a multiple of KS).
-template <int PHASE>
-__global__ __launch_bounds__(256) void ns_f32_kernel(const MatDesc* __restrict__ descs, int n,
-                                                     const int32_t* __restrict__ prefix, int it,
-                                                     float ca, float cb, float cc) {
-    __shared__ float Ps[KS][T + 4];
-    __shared__ float Qs[KS][T + 4];
-    const F32Tile<PHASE> tl = f32_tile<PHASE>(descs, n, prefix, it);
-    const int t = threadIdx.x;
-    const int ty = t >> 4, tx = t & 15;
-    const int lrow = t >> 2, lk = (t & 3) * 4;
-    const float* Pr = tl.P + (int64_t)(tl.ti * T + lrow) * tl.ldp + lk;
-    const float* Qr = tl.Q + (int64_t)(tl.tj * T + lrow) * tl.ldq + lk;
-
-    float acc[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-
-    for (int k0 = 0; k0 < tl.K; k0 += KS) {
-        const float4 pv = gld(reinterpret_cast<const float4*>(Pr + k0));
-        const float4 qv = gld(reinterpret_cast<const float4*>(Qr + k0));
-        __syncthreads();
-        Ps[lk + 0][lrow] = pv.x; Ps[lk + 1][lrow] = pv.y; Ps[lk + 2][lrow] = pv.z; Ps[lk + 3][lrow] = pv.w;
-        Qs[lk + 0][lrow] = qv.x; Qs[lk + 1][lrow] = qv.y; Qs[lk + 2][lrow] = qv.z; Qs[lk + 3][lrow] = qv.w;
-        __syncthreads();
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            float a[4], b[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = Ps[kk][ty * 4 + r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) b[c] = Qs[kk][tx * 4 + c];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(a[r], b[c], acc[r][c]);
-        }
-    }
-    f32_epilogue<PHASE>(tl, acc, it, ca, cb, cc);
-}
-
 // K of at most KMAX: every thread issues the loads of the tile's whole K
 // extent at once, they go to LDS transposed, and after one barrier the
-// product runs from LDS.  The slab loop above waits for one load latency per
-// 16 K-steps; on a small matrix that chain, not the arithmetic, sets the
-// launch time.
+// product runs from LDS (on a tiny matrix the load latency, not the
+// arithmetic, sets the launch time).
 template <int PHASE, int KMAX>
 __global__ __launch_bounds__(256) void ns_f32_shortk_kernel(const MatDesc* __restrict__ descs, int n,
                                                             const int32_t* __restrict__ prefix, int it,
@@ -219,17 +175,19 @@ __global__ __launch_bounds__(256) void ns_f32_shortk_kernel(const MatDesc* __res
 }  // namespace
 
 // The kernel for a launch whose largest K is kmax (the planner's largest n'
-// or m' of the class, so every tile's K fits the chosen KMAX).
+// or m' of the class): the FMA kernel staging the whole K up to 64 (a launch
+// of tiny matrices only), else the matrix-core kernel.  Measured: the
+// 256 x 256 matrix's launches 16.2-17.0 us with the FMA kernels, 8.9-9.2 us
+// on the matrix cores; 2500 matrices of at most 32 x 32, the step 0.73-0.77
+// ms with the FMA kernel, 0.78-0.80 ms on the matrix cores.
 template <int PHASE>
 hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total, int it, int kmax,
                       float a, float b, float c, hipStream_t st) {
-    if (kmax <= 64)
+    if (kmax <= 64) {
         ns_f32_shortk_kernel<PHASE, 64><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
-    else if (kmax <= 256)
-        ns_f32_shortk_kernel<PHASE, 256><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
-    else
-        return launch_f32_mfma(PHASE, d, n, prefix, total, it, a, b, c, st);
-    return hipGetLastError();
+        return hipGetLastError();
+    }
+    return launch_f32_mfma(PHASE, d, n, prefix, total, it, a, b, c, st);
 }
 
 hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, hipStream_t st) {

@@ -103,10 +103,10 @@ hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* pref
                                    const XcdSplit& xs, int it, int strip, int next_gram, float a, float b,
                                    float c, hipStream_t st);
 
-// fp32 class (every tile of the symmetric products; p.gram == p.tri).
+// fp32 class (p.gram == p.tri: the prefix counts every tile of the square).
 // kmax: the largest K of the launch's matrices (n' for the Gram, m' for the
-// polynomial and the update); up to 256 the whole K extent of a tile is
-// staged in LDS at once
+// polynomial and the update); up to 64 an FMA kernel stages a tile's whole K
+// extent in LDS at once, above that the launch runs on the matrix cores
 hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax,
                            hipStream_t st);
 hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, int kmax, float b, float c,
