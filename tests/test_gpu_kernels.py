@@ -169,6 +169,13 @@ def test_step_single_matrix_f32(shape):
     _run_and_compare([shape], dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=7)
 
 
+def test_fp32_iteration_on_larger_matrices():
+    # the fp32 iteration on the matrix cores: hundreds of triangle tiles with
+    # mirrored stores, K up to 2048, both orientations, at the fp32 bound
+    _run_and_compare([(1536, 2048), (2048, 1536), (704, 1984)], dict(BASE_HP, ns_dtype="fp32"),
+                     TOL_O_F32, seed=19)
+
+
 def test_step_mixed_batch_bf16():
     _run_and_compare(MIXED, BASE_HP, TOL_O_BF16, seed=11)
 
