@@ -1305,6 +1305,59 @@ __device__ __forceinline__ void epilogue_f32(const f32x16 (&acc)[C::FM][C::FN], 
 
 using F32Cfg = Cfg<64, 64, 2, 2, 64, 2>;
 
+// Operands and epilogue of one fp32 tile in phase PHASE (mirror: an
+// off-diagonal tile of a symmetric product, also stored transposed).
+template <int PHASE>
+__device__ __forceinline__ void f32_operands(const MatDesc& d, int it, float ca, float cb, float cc, bool mirror,
+                                             const float*& P, const float*& Q, int64_t& ld, int& K,
+                                             EpiF32& ep) {
+    const int64_t mp = d.mp, np = d.np;
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
+    ep.coef_acc = 1.f;
+    ep.post = 1.f;
+    if (PHASE == GRAM) {
+        P = Q = reinterpret_cast<const float*>(d.x[it & 1]);
+        ld = np;
+        K = (int)np;
+        const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
+        ep.coef_acc = s * s;
+        ep.out = reinterpret_cast<float*>(d.a);
+        ep.ld_out = mp;
+        ep.outT = mirror ? ep.out : nullptr;
+        ep.ld_outT = mp;
+    } else if (PHASE == POLY) {
+        P = Q = reinterpret_cast<const float*>(d.a);
+        ld = mp;
+        K = (int)mp;
+        ep.E = P;
+        ep.ld_e = mp;
+        ep.coef_e = cb;
+        ep.coef_acc = cc;
+        ep.out = reinterpret_cast<float*>(d.b);
+        ep.ld_out = mp;
+        ep.outT = mirror ? ep.out : nullptr;
+        ep.ld_outT = mp;
+    } else {
+        P = reinterpret_cast<const float*>(d.b);
+        Q = reinterpret_cast<const float*>(d.xt[it & 1]);
+        ld = mp;
+        K = (int)mp;
+        ep.E = reinterpret_cast<const float*>(d.x[it & 1]);
+        ep.ld_e = np;
+        ep.coef_e = ca;
+        ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
+        ep.out = reinterpret_cast<float*>(d.x[(it + 1) & 1]);
+        ep.ld_out = np;
+        ep.outT = reinterpret_cast<float*>(d.xt[(it + 1) & 1]);
+        ep.ld_outT = mp;
+    }
+}
+
+
 // One fp32 tile per workgroup, over the class's prefix of (full-square or
 // update) tiles.
 template <int PHASE>
@@ -1340,53 +1393,118 @@ __global__ __launch_bounds__(F32Cfg::NT) void ns_f32_mfma_kernel(const MatDesc* 
     int64_t ld;
     int K;
     EpiF32 ep;
-    ep.outT = nullptr;
-    ep.ld_outT = 0;
-    ep.E = nullptr;
-    ep.ld_e = 0;
-    ep.coef_e = 0.f;
-    ep.coef_acc = 1.f;
-    ep.post = 1.f;
-    if (PHASE == GRAM) {
-        P = Q = reinterpret_cast<const float*>(d.x[it & 1]);
-        ld = np;
-        K = (int)np;
-        const float s = (it == 0) ? gld(d.inv_norm) : 1.f;
-        ep.coef_acc = s * s;
-        ep.out = reinterpret_cast<float*>(d.a);
-        ep.ld_out = mp;
-        ep.outT = ti == tj ? nullptr : ep.out;
-        ep.ld_outT = mp;
-    } else if (PHASE == POLY) {
-        P = Q = reinterpret_cast<const float*>(d.a);
-        ld = mp;
-        K = (int)mp;
-        ep.E = P;
-        ep.ld_e = mp;
-        ep.coef_e = cb;
-        ep.coef_acc = cc;
-        ep.out = reinterpret_cast<float*>(d.b);
-        ep.ld_out = mp;
-        ep.outT = ti == tj ? nullptr : ep.out;
-        ep.ld_outT = mp;
-    } else {
-        P = reinterpret_cast<const float*>(d.b);
-        Q = reinterpret_cast<const float*>(d.xt[it & 1]);
-        ld = mp;
-        K = (int)mp;
-        ep.E = reinterpret_cast<const float*>(d.x[it & 1]);
-        ep.ld_e = np;
-        ep.coef_e = ca;
-        ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
-        ep.out = reinterpret_cast<float*>(d.x[(it + 1) & 1]);
-        ep.ld_out = np;
-        ep.outT = reinterpret_cast<float*>(d.xt[(it + 1) & 1]);
-        ep.ld_outT = mp;
-    }
+    f32_operands<PHASE>(d, it, ca, cb, cc, ti != tj, P, Q, ld, K, ep);
     const int64_t r0 = (int64_t)ti * C::BM, c0 = (int64_t)tj * C::BN;
     f32x16 acc[C::FM][C::FN];
     gemm_mainloop_f32<C>(P + r0 * ld, ld, Q + c0 * ld, ld, K, st, acc);
     epilogue_f32<C>(acc, r0, c0, ep, reinterpret_cast<float*>(lds_arr(st, 0)));
+}
+
+// fp32 launches of short K (up to KMAX, e.g. one 256 x 256 matrix): a tile of
+// 64 leaves most compute units idle and runs its whole K on one.  Here each
+// 64-tile of the class's prefix is four workgroups of 32 x 32, and the four
+// waves of a workgroup split K: every wave multiplies its quarter of the
+// slabs into its own 32 x 32 accumulator, then the four partial tiles are
+// summed through LDS in wave order.  The tile's whole K is copied at once.
+struct F32SkCopy {  // slab geometry for load_slab / read_frag: 128-byte rows
+    static constexpr int BK = 64, CH = 8, RPI = 8, NW = 4;
+};
+
+template <int PHASE, int KMAX>
+__global__ __launch_bounds__(256) void ns_f32_splitk_kernel(const MatDesc* __restrict__ descs, int n,
+                                                            const int32_t* __restrict__ prefix, int it,
+                                                            float ca, float cb, float cc) {
+    using CP = F32SkCopy;
+    constexpr int TB = 32, NSL = KMAX / 32;  // tile edge, fp32 slabs of 32
+    static_assert(KMAX % 64 == 0, "whole slab pairs");
+    __shared__ __attribute__((aligned(1024))) uint16_t lp[NSL * TB * CP::BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t lq[NSL * TB * CP::BK];
+    __shared__ __attribute__((aligned(16))) float red[4 * TB * TB];
+    const int t64 = blockIdx.x >> 2, q = blockIdx.x & 3;
+    const int mi = find_matrix(prefix, n, t64);
+    const MatDesc& d = descs[mi];
+    const int lt = t64 - prefix[mi];
+    int ti, tj;
+    if (PHASE == UPDATE) {
+        const int tcols = (int)(d.np / kTileF32);
+        ti = lt / tcols;
+        tj = lt - ti * tcols;
+    } else {
+        // lower triangle of 64-tiles (the rest of the square's prefix idle),
+        // and of a diagonal 64-tile the quarters on and below its diagonal
+        const int T = (int)(d.mp / kTileF32);
+        if (lt >= T * (T + 1) / 2) return;
+        tri_index(lt, ti, tj);
+        if (ti == tj && (q >> 1) < (q & 1)) return;
+    }
+    ti = 2 * ti + (q >> 1);
+    tj = 2 * tj + (q & 1);
+    const float *P, *Q;
+    int64_t ld;
+    int K;
+    EpiF32 ep;
+    f32_operands<PHASE>(d, it, ca, cb, cc, ti != tj, P, Q, ld, K, ep);
+    const int64_t r0 = (int64_t)ti * TB, c0 = (int64_t)tj * TB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int frow = lane & 31, khalf = lane >> 5;
+    const int ns = K / 32;  // slabs of this tile (at most NSL)
+    {
+        const uint16_t* P0 = reinterpret_cast<const uint16_t*>(P + r0 * ld);
+        const uint16_t* Q0 = reinterpret_cast<const uint16_t*>(Q + c0 * ld);
+        for (int sl = 0; sl < ns; ++sl) {
+            load_slab<CP, TB>(P0 + 64 * sl, 2 * ld, lp + sl * TB * CP::BK, wave, lane);
+            load_slab<CP, TB>(Q0 + 64 * sl, 2 * ld, lq + sl * TB * CP::BK, wave, lane);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const int s0 = wave * ns / 4, s1 = (wave + 1) * ns / 4;
+    for (int sl = s0; sl < s1; ++sl) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const f32x4 a = __builtin_bit_cast(f32x4, read_frag<CP>(lp + sl * TB * CP::BK, frow, 2 * kk + khalf));
+            const f32x4 b = __builtin_bit_cast(f32x4, read_frag<CP>(lq + sl * TB * CP::BK, frow, 2 * kk + khalf));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[t], b[t], acc, 0, 0, 0);
+        }
+    }
+    // partial tiles to LDS (row 8 (r >> 2) + 4 khalf + (r & 3), column frow), summed in wave order
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave * TB * TB + (8 * (r >> 2) + 4 * khalf + (r & 3)) * TB + frow] = acc[r];
+    __syncthreads();
+    const int row = threadIdx.x >> 3, col = (threadIdx.x & 7) * 4;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int o = row * TB + col + e;
+        v[e] = ((red[o] + red[TB * TB + o]) + red[2 * TB * TB + o]) + red[3 * TB * TB + o];
+    }
+    if (ep.E) {
+        const float4 e4 = gld(reinterpret_cast<const float4*>(ep.E + (r0 + row) * ep.ld_e + c0 + col));
+        const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ep.post * (ep.coef_acc * v[e] + ep.coef_e * ev[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ep.post * (ep.coef_acc * v[e]);
+    }
+    gst(reinterpret_cast<float4*>(ep.out + (r0 + row) * ep.ld_out + c0 + col), make_float4(v[0], v[1], v[2], v[3]));
+    if (ep.outT) {
+        // the transpose through the first partial tile's LDS (read by now:
+        // a barrier after every thread's sums)
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(col + e) * (TB + 1) + row] = v[e];
+        __syncthreads();
+        float w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = red[row * (TB + 1) + col + e];
+        gst(reinterpret_cast<float4*>(ep.outT + (c0 + row) * ep.ld_outT + r0 + col),
+            make_float4(w[0], w[1], w[2], w[3]));
+    }
 }
 
 // single-matrix variants for the test hooks
@@ -1578,7 +1696,16 @@ hipError_t launch_update_bf16_single(const void* X, const void* B, void* Xo, int
 }
 
 hipError_t launch_f32_mfma(int phase, const MatDesc* d, int n, const int32_t* prefix, int total, int it,
-                           float a, float b, float c, hipStream_t st) {
+                           int kmax, float a, float b, float c, hipStream_t st) {
+    if (kmax <= 256) {
+        if (phase == GRAM)
+            ns_f32_splitk_kernel<GRAM, 256><<<4 * total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+        else if (phase == POLY)
+            ns_f32_splitk_kernel<POLY, 256><<<4 * total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+        else
+            ns_f32_splitk_kernel<UPDATE, 256><<<4 * total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
+        return hipGetLastError();
+    }
     if (phase == GRAM)
         ns_f32_mfma_kernel<GRAM><<<total, F32Cfg::NT, 0, st>>>(d, n, prefix, it, a, b, c);
     else if (phase == POLY)

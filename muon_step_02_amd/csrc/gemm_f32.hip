@@ -187,7 +187,7 @@ hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total,
         ns_f32_shortk_kernel<PHASE, 64><<<total, 256, 0, st>>>(d, n, prefix, it, a, b, c);
         return hipGetLastError();
     }
-    return launch_f32_mfma(PHASE, d, n, prefix, total, it, a, b, c, st);
+    return launch_f32_mfma(PHASE, d, n, prefix, total, it, kmax, a, b, c, st);
 }
 
 hipError_t launch_gram_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, hipStream_t st) {

@@ -113,11 +113,13 @@ hipError_t launch_poly_f32(const MatDesc* d, int n, Prefix p, int total, int kma
                            hipStream_t st);
 hipError_t launch_update_f32(const MatDesc* d, int n, Prefix p, int total, int it, int kmax, float a,
                              hipStream_t st);
-// the fp32 products on the matrix cores (64 x 64 tiles, K a multiple of 32),
-// for launches whose K exceeds what the FMA kernels stage whole; phase: 0
-// Gram, 1 polynomial, 2 update; prefix and total as for the FMA launches
+// the fp32 products on the matrix cores, for launches whose K exceeds what
+// the FMA kernel stages whole; phase: 0 Gram, 1 polynomial, 2 update; prefix
+// and total as for the FMA launches (64-tiles); kmax as above: up to 256 each
+// 64-tile is four workgroups of 32 x 32 that split K over their waves, above
+// that one workgroup per 64-tile pipelines its K
 hipError_t launch_f32_mfma(int phase, const MatDesc* d, int n, const int32_t* prefix, int total, int it,
-                           float a, float b, float c, hipStream_t st);
+                           int kmax, float a, float b, float c, hipStream_t st);
 
 // single-phase test hooks (one matrix, caller buffers)
 hipError_t launch_gram_bf16_single(const void* X, void* A, int m, int n, int64_t ldx, int64_t lda,
