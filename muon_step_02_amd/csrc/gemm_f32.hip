@@ -176,10 +176,11 @@ __global__ __launch_bounds__(256) void ns_f32_shortk_kernel(const MatDesc* __res
 
 // The kernel for a launch whose largest K is kmax (the planner's largest n'
 // or m' of the class): the FMA kernel staging the whole K up to 64 (a launch
-// of tiny matrices only), else the matrix-core kernel.  Measured: the
-// 256 x 256 matrix's launches 16.2-17.0 us with the FMA kernels, 8.9-9.2 us
-// on the matrix cores; 2500 matrices of at most 32 x 32, the step 0.73-0.77
-// ms with the FMA kernel, 0.78-0.80 ms on the matrix cores.
+// of tiny matrices only), else the matrix-core kernels.  Measured: the
+// 256 x 256 matrix's launches 16.2-17.0 us with the FMA kernels, 5.1-5.4 us
+// on the matrix cores (K split four ways); 2500 matrices of at most 32 x 32,
+// the step 0.73-0.77 ms with the FMA kernel, 0.78-0.80 ms on the matrix
+// cores.
 template <int PHASE>
 hipError_t launch_f32(const MatDesc* d, int n, const int32_t* prefix, int total, int it, int kmax,
                       float a, float b, float c, hipStream_t st) {
