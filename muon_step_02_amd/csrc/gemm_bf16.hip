@@ -360,17 +360,13 @@ __device__ __forceinline__ void load_e_band(const Epi& ep, int64_t row0, int64_t
 // E is loaded one band ahead so its latency hides behind the LDS work.
 // LIGHT: the band barriers carry no memory fence, for a caller that has
 // global->LDS copies in flight into other arrays which the epilogue must not
-// wait for.  XO: the stored bf16 tile is also written to LDS as two row
-// slabs of 64 columns each (xo[0], xo[1]; layout of load_slab), for a
-// product of the tile with itself.
+// wait for.
 // (wm, wn): the wave's position in the WM x WN grid; frow = lane & 31,
 // khalf = lane >> 5.
-template <class C, bool HAS_E, bool F32OUT, bool LIGHT = false, bool XO = false>
+template <class C, bool HAS_E, bool F32OUT, bool LIGHT = false>
 __device__ __forceinline__ void epilogue_bands(const f32x16 (&acc)[C::FM][C::FN], int64_t row0,
                                                int64_t col0, const Epi& ep, float* sb, int wm,
-                                               int wn, int frow, int khalf,
-                                               uint16_t* const* xo = nullptr) {
-    static_assert(!XO || (C::BN == 128 && C::BK == 64 && !F32OUT), "two 64-column slabs");
+                                               int wn, int frow, int khalf) {
     constexpr int QN = (C::RB * C::BN / 8) / C::NT;  // 16-byte chunks per thread per band
     uint4 ecur[QN], enxt[QN];
     if (HAS_E) load_e_band<C, QN>(ep, row0, col0, 0, ecur);
@@ -432,11 +428,6 @@ __device__ __forceinline__ void epilogue_bands(const f32x16 (&acc)[C::FM][C::FN]
             o.z = pack2(v[4], v[5]);
             o.w = pack2(v[6], v[7]);
             store_out(ep.out + brow * ep.ld_out + col0, (uint32_t)(rr * ep.ld_out + c8) * 2u, o);
-            if constexpr (XO) {
-                const int row = band * C::RB + rr;
-                const int lch = (c8 & 63) >> 3;
-                *reinterpret_cast<uint4*>(xo[c8 >> 6] + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3)) = o;
-            }
             if (ep.outT) {
                 *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8)) = make_float4(v[0], v[1], v[2], v[3]);
                 *reinterpret_cast<float4*>(sb + sbi<C>(rr, c8) + 4) = make_float4(v[4], v[5], v[6], v[7]);
