@@ -176,6 +176,14 @@ def test_fp32_iteration_on_larger_matrices():
                      TOL_O_F32, seed=19)
 
 
+@pytest.mark.parametrize("shapes", [[(100, 150)], [(150, 100), (128, 192)], [(192, 130), (64, 200)]],
+                         ids=["K 128 and 192", "K 128 and 192, two matrices", "K 192 and 256"])
+def test_fp32_iteration_short_k(shapes):
+    # launches whose K is at most 256 split each 64-tile into four 32 x 32
+    # workgroups that divide K over their waves: K of 2, 3 and 4 slab pairs
+    _run_and_compare(shapes, dict(BASE_HP, ns_dtype="fp32"), TOL_O_F32, seed=23)
+
+
 def test_step_mixed_batch_bf16():
     _run_and_compare(MIXED, BASE_HP, TOL_O_BF16, seed=11)
 
