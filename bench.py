@@ -190,12 +190,17 @@ def main():
 
     # per-phase algorithmic work per launch
     per_launch_flops = {"gram": 0.0, "poly": 0.0, "update": 0.0}
+    # algorithmic bytes of one update launch: X read and the next X written
+    # (m x n each) and B read (m x m), in the iteration's element size
+    ns_elem = 4 if hpd["ns_dtype"] == "fp32" else 2
+    update_bytes = 0.0
     el = 0
     for r, c in wl.muon_shapes():
         m, n = min(r, c), max(r, c)
         per_launch_flops["gram"] += m * m * n
         per_launch_flops["poly"] += m ** 3
         per_launch_flops["update"] += 2 * m * m * n
+        update_bytes += (2 * m * n + m * m) * ns_elem
         el += r * c
     peak_mm = PEAK_F32_TFLOPS if hpd["ns_dtype"] == "fp32" else PEAK_BF16_TFLOPS
     # Per phase and Newton-Schulz iteration: every launch of the phase (one
@@ -247,6 +252,16 @@ def main():
                 "launches_per_iteration": gemm[dom]["launches_per_iteration"],
                 "timing": "HIP events around every launch, in a second pass of the same steps "
                           "after the timed region"}
+    # An update whose arithmetic intensity lies below the ridge point (short
+    # side m: about m/2 flop per byte in bf16) is bound by HBM, not by the
+    # matrix cores: per-head blocks (m = 128) are.  Report that roofline then.
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if dom == "update" and per_launch_flops["update"] / update_bytes < ridge and dom_avg_ms > 0:
+        gbs = update_bytes / (dom_avg_ms * 1e-3) / 1e9
+        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "per_launch_bytes": update_bytes,
+                         "arithmetic_intensity": round(per_launch_flops["update"] / update_bytes, 1),
+                         "ridge": round(ridge, 1)})
 
     out = {
         "metric": "Muon step TFLOP/s (algorithmic, bf16 Newton-Schulz) and matrices/s",
