@@ -46,11 +46,25 @@ def parse():
     return ap.parse_args()
 
 
-def _traffic_record(kernel):
+def hbm_roofline(flops, nbytes, avg_ms, peak_tflops, peak_gbs=PEAK_HBM_GBS):
+    """The HBM roofline of a launch doing `flops` on `nbytes` of algorithmic
+    traffic in avg_ms, if its arithmetic intensity lies below the ridge point
+    (peak flop / peak bandwidth); None when the matrix cores bound it."""
+    ridge = peak_tflops * 1e12 / (peak_gbs * 1e9)
+    if nbytes <= 0 or avg_ms <= 0 or flops / nbytes >= ridge:
+        return None
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": peak_gbs, "unit": "GB/s",
+            "frac": round(gbs / peak_gbs, 4), "per_launch_bytes": nbytes,
+            "arithmetic_intensity": round(flops / nbytes, 1), "ridge": round(ridge, 1)}
+
+
+def _traffic_record(kernel, root=None):
     """HBM traffic per launch measured with rocprofv3 counters, if the record
     in profiles/ was taken on the current source of the kernel."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_%s.md" % kernel)
+    root = root or ROOT
+    path = os.path.join(root, "profiles", "traffic_%s.md" % kernel)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -58,7 +72,7 @@ def _traffic_record(kernel):
     b = re.search(r"^bytes_per_launch:\s*([0-9.eE+]+)", txt, flags=re.M)
     if not m or not b:
         return None
-    src = os.path.join(ROOT, "muon_step_02_amd", "csrc", "gemm_bf16.hip")
+    src = os.path.join(root, "muon_step_02_amd", "csrc", "gemm_bf16.hip")
     h = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if h != m.group(1):
         return None
@@ -255,13 +269,9 @@ def main():
     # An update whose arithmetic intensity lies below the ridge point (short
     # side m: about m/2 flop per byte in bf16) is bound by HBM, not by the
     # matrix cores: per-head blocks (m = 128) are.  Report that roofline then.
-    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if dom == "update" and per_launch_flops["update"] / update_bytes < ridge and dom_avg_ms > 0:
-        gbs = update_bytes / (dom_avg_ms * 1e-3) / 1e9
-        roofline.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "per_launch_bytes": update_bytes,
-                         "arithmetic_intensity": round(per_launch_flops["update"] / update_bytes, 1),
-                         "ridge": round(ridge, 1)})
+    hbm_rf = hbm_roofline(per_launch_flops["update"], update_bytes, dom_avg_ms, peak_mm) if dom == "update" else None
+    if hbm_rf:
+        roofline.update(hbm_rf)
 
     out = {
         "metric": "Muon step TFLOP/s (algorithmic, bf16 Newton-Schulz) and matrices/s",

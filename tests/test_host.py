@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -234,3 +235,37 @@ def test_xcd_split_covers_every_tile_once_with_balanced_work(tmp_path):
                     "-Wl,-rpath," + libdir], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_bench_roofline_choice_and_traffic_record(tmp_path):
+    # bench.py's helpers: the HBM roofline applies below the ridge point only,
+    # and a traffic record counts only for the kernel source it was taken on
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    m, n = 128, 7168                       # a per-head block: about 63 flop per byte
+    flops, nbytes = 2 * m * m * n, (2 * m * n + m * m) * 2
+    r = b.hbm_roofline(flops, nbytes, avg_ms=0.5, peak_tflops=2500.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - nbytes / 0.5e-3 / 1e9) < 0.1
+    assert abs(r["frac"] - r["achieved"] / 8000.0) < 1e-3
+    m = n = 4096                           # the headline's update: matrix-core bound
+    assert b.hbm_roofline(2 * m * m * n, (2 * m * n + m * m) * 2, 0.1, 2500.0) is None
+    src = tmp_path / "muon_step_02_amd" / "csrc"
+    src.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (src / "gemm_bf16.hip").write_bytes(b"kernel source A")
+    import hashlib
+    sha = hashlib.sha256(b"kernel source A").hexdigest()
+    rec = tmp_path / "profiles" / "traffic_k.md"
+    rec.write_text("text\nsource_sha256: %s\nbytes_per_launch: 1.5e+09\n" % sha)
+    assert b._traffic_record("k", root=str(tmp_path)) == 1.5e9
+    (src / "gemm_bf16.hip").write_bytes(b"kernel source B")
+    assert b._traffic_record("k", root=str(tmp_path)) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
