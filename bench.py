@@ -259,7 +259,9 @@ def main():
 
     dom_avg_ms = gemm[dom]["avg_ms"]
     traffic = _traffic_record("update_bf16_headline") if (dom == "update" and args.workload == "headline") else None
-    roofline = {"bound": "mfma", "kernel": "ns_update (X <- B X, B = aI + bA + cAA)" if dom == "update" else dom,
+    upd_name = ("ns_update (X <- B X, B = aI + bA + cAA)" if hpd["ns_dtype"] == "bf16"
+                else "fp32 update (X <- aX + BX, B = bA + cAA)")
+    roofline = {"bound": "mfma", "kernel": upd_name if dom == "update" else dom,
                 "achieved": gemm[dom]["tflops"], "peak": peak_mm, "unit": "TFLOP/s",
                 "frac": gemm[dom]["frac"], "traffic": traffic,
                 "per_launch_flops": per_launch_flops[dom], "avg_launch_ms": dom_avg_ms,
