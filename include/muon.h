@@ -221,7 +221,9 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n,
  * and clears the record.  Launches on the two streams may overlap in time,
  * and their durations are added all the same.  Timing does not change what the
  * kernels compute.  Phases: 0 momentum, 1 norm, 2 gram, 3 poly, 4 update,
- * 5 apply, 6 adamw. */
+ * 5 apply, 6 adamw (matrices whose short side is at most 128, when their
+ * update runs in strips, form the polynomial and the later Gram parts inside
+ * the update launches: phase 4, with no phase-3 launch for them). */
 #define MUON_NUM_PHASES 7
 typedef struct {
     float ms[MUON_NUM_PHASES];     /* summed launch durations per phase */
