@@ -1,4 +1,6 @@
-// bf16 MFMA kernels of the quintic Newton-Schulz iteration (gfx950).
+// MFMA kernels of the quintic Newton-Schulz iteration (gfx950): the bf16
+// products, and at the end of the file the fp32 option's products on the same
+// slab machinery (v_mfma_f32_32x32x2f32).
 //
 // One iteration X <- a X + b (X X^T) X + c (X X^T)^2 X is computed on the
 // small Gram as three products ("About Muon: Why Not Adam", kiungsong.github.io,
