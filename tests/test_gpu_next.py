@@ -223,11 +223,15 @@ def test_mixed_class_call_equals_one_call_per_class():
             assert torch.equal(Wa[i], Wb[i]), (step, i, "W")
 
 
-def test_small_class_update_in_strips():
+@pytest.mark.parametrize("hpd", [BASE_HP, dict(BASE_HP, steps=3, coeffs=[3.0, -3.2, 1.2, 3.4445, -4.7750, 2.0315,
+                                                                  1.875, -1.25, 0.375])],
+                         ids=["5 steps", "3 steps, schedule"])
+def test_small_class_update_in_strips(hpd):
     # 8 blocks of 100 x 4900 and 8 of 4900 x 100 (transposed): 16 x 39 column
     # tiles of 128 in the small class, more than two workgroups per compute
     # unit can take at once, so the update runs two tiles per workgroup and
-    # the last strip of every matrix holds one tile.
+    # the last strip of every matrix holds one tile.  Each strip forms its
+    # matrix's B itself, with the iteration's coefficients.
     from harness import TOL_BLOCK_BF16, check_output
     shapes = [(100, 4900)] * 8 + [(4900, 100)] * 8
     W = [_weight(r, c, 80 + i) for i, (r, c) in enumerate(shapes)]
@@ -236,9 +240,9 @@ def test_small_class_update_in_strips():
     O = [torch.empty(r, c, device=DEV) for r, c in shapes]
     ins = [(f64(w), f64(g)) for w, g in zip(W, G)]
     run_muon_step([mu.muon_matrix(W[i], G[i], M[i], update_out=O[i]) for i in range(len(shapes))],
-                  hp_from(BASE_HP))
+                  hp_from(hpd))
     torch.cuda.synchronize()
-    kw = oracle_kwargs(BASE_HP)
+    kw = oracle_kwargs(hpd)
     for i, (W0, G0) in enumerate(ins):
         Wr, Mr, Or = oracle.muon_matrix_step(W0, G0, np.zeros_like(W0), **kw)
         check_output(f64(O[i]), Or, TOL_O_BF16, TOL_BLOCK_BF16, what="strip matrix %d" % i)
