@@ -258,7 +258,10 @@ def main():
                         "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
     dom_avg_ms = gemm[dom]["avg_ms"]
-    traffic = _traffic_record("update_bf16_headline") if (dom == "update" and args.workload == "headline") else None
+    # HBM bytes per update launch from rocprofv3 counters, where a record for
+    # this workload and the current kernel source is committed
+    records = {"headline": "update_bf16_headline", "perhead": "update_strip_perhead"}
+    traffic = _traffic_record(records[args.workload]) if (dom == "update" and args.workload in records) else None
     upd_name = ("ns_update (X <- B X, B = aI + bA + cAA)" if hpd["ns_dtype"] == "bf16"
                 else "fp32 update (X <- aX + BX, B = bA + cAA)")
     roofline = {"bound": "mfma", "kernel": upd_name if dom == "update" else dom,
