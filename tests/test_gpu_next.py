@@ -285,3 +285,32 @@ def test_per_head_gram_parts_from_update_strips(hpd):
                                                        TOL_O_BF16), (step, h)
             # carry the GPU's own state, so each step is checked on its own
             ref[h] = [f64(Wf[sl]), f64(Mf[sl])]
+
+
+def test_per_head_column_blocks_fused_strips():
+    # Column blocks of a (3584, 64 x 128) tensor: 64 strided views of 3584 x 128
+    # (leading dimension 8192), tall, so each is transposed to 128 x 3584: the
+    # small class with 7 Gram parts and 7 strips per block, the fused strip
+    # update, the momentum and apply transposing through LDS, and the other
+    # columns of the tensor untouched.  Sampled blocks against the oracle.
+    heads, dh, rows = 64, 128, 3584
+    Wf = _weight(rows, heads * dh, 31)
+    Gf = _grad(rows, heads * dh, 32)
+    Mf = torch.zeros(rows, heads * dh, device=DEV)
+    O = [torch.empty(rows, dh, device=DEV) for _ in range(heads)]
+    W0f = Wf.clone()
+    mats = [mu.muon_matrix(Wf[:, h * dh:(h + 1) * dh], Gf[:, h * dh:(h + 1) * dh], Mf[:, h * dh:(h + 1) * dh],
+                           update_out=O[h]) for h in range(heads - 1)]  # the last block stays untouched
+    run_muon_step(mats, hp_from(BASE_HP))
+    torch.cuda.synchronize()
+    kw = oracle_kwargs(BASE_HP)
+    for h in [0, 1, 7, 31, 32, 62]:
+        sl = slice(h * dh, (h + 1) * dh)
+        W0, G0 = f64(W0f[:, sl]), f64(Gf[:, sl])
+        Wr, Mr, Or = oracle.muon_matrix_step(W0, G0, np.zeros_like(W0), **kw)
+        assert relF(f64(O[h]), Or) <= TOL_O_BF16, h
+        assert relF(f64(Mf[:, sl]), Mr) <= TOL_STATE, h
+        assert relF(f64(Wf[:, sl]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(rows, dh), Or, Wr,
+                                                       TOL_O_BF16), h
+    last = slice((heads - 1) * dh, heads * dh)
+    assert torch.equal(Wf[:, last], W0f[:, last]) and torch.count_nonzero(Mf[:, last]) == 0
