@@ -588,6 +588,32 @@ __device__ __forceinline__ void tri_index(int lt, int& ti, int& tj) {
     tj = lt - t * (t + 1) / 2;
 }
 
+// The Gram and polynomial launches take a matrix's triangle tiles in blocked
+// order: super-rows of S tile-rows, and within one the S x S blocks left of
+// the diagonal (row-major), then the diagonal block's triangle.  A super-row
+// holds the same tiles as S rows of the row-major order, permuted, so a window
+// of concurrent tiles on an XCD touches fewer operand row panels (measured on
+// the Llama-style layer: Gram and polynomial 3% faster; unchanged on 4096^2
+// batches, and the same order as row-major up to S tile-rows).
+__device__ __forceinline__ void tri_index_blocked(int lt, int T, int& ti, int& tj) {
+    constexpr int S = 8;
+    int t, u;
+    tri_index(lt, t, u);
+    const int I = t / S;
+    const int r = min(S, T - I * S);  // tile-rows in super-row I
+    const int loc = lt - (I * S) * (I * S + 1) / 2;
+    if (loc < r * S * I) {
+        const int J = loc / (r * S), l2 = loc - J * r * S;
+        ti = I * S + l2 / S;
+        tj = J * S + l2 % S;
+    } else {
+        int a, b;
+        tri_index(loc - r * S * I, a, b);
+        ti = I * S + a;
+        tj = I * S + b;
+    }
+}
+
 // Update tiles in groups of kUpdGroup tile-rows: within a group the column
 // index advances slowest, so concurrently running tiles reuse a few B
 // row-panels and X column-panels.
@@ -617,7 +643,7 @@ __global__ __launch_bounds__(C::NT) void ns_sym_kernel(const MatDesc* __restrict
     const int mi = find_matrix(prefix, n, tile);
     const MatDesc& d = descs[mi];
     int ti, tj;
-    tri_index(tile - prefix[mi], ti, tj);
+    tri_index_blocked(tile - prefix[mi], (int)(d.mp / C::BM), ti, tj);
     // a quarter above the diagonal of a diagonal tile is the mirror of the
     // quarter below it
     if (q >= 0 && ti == tj && (q >> 1) < (q & 1)) return;
