@@ -313,7 +313,8 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                     return launch_update_strip_bf16(dc, C.count,
                                                     reinterpret_cast<const int32_t*>(ws + C.off_pstrip),
                                                     C.xs_strip, it, C.strip,
-                                                    C.fuse_gram && it + 1 < hp->ns_steps, a, b, c, sk);
+                                                    C.fuse_gram && it + 1 < hp->ns_steps, C.stream, a, b,
+                                                    c, sk);
                 return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }

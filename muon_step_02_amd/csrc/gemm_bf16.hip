@@ -43,6 +43,8 @@
 // (matrix, tile) through prefix sums of tiles per matrix.
 #include "muon_internal.h"
 
+#include <type_traits>
+
 namespace muon {
 
 namespace {
@@ -1155,6 +1157,368 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
 }
 
+// The streaming strip kernel's epilogue, first half: the tile held in rows
+// (mfma_frags_rows) is scaled, rounded to bf16 and written to LDS as two row
+// slabs of 64 columns (x0, x1, two arrays; load_slab's layout).  The
+// streaming kernel gives wave (wm, wn) the
+// column blocks 64 jj + 32 wn .. + 31 (jj = 0, 1), so block jj lies in slab
+// jj whatever the wave and every write names its array at compile time.
+// Lanes l and l + 32 hold the two halves (four columns each) of the same
+// 8-column chunks of one row; v_permlane32_swap trades them so that every
+// lane writes one whole chunk of 16 bytes: lane l chunk g, lane l + 32 chunk
+// g + 1, for g = 0, 2.  (Pairs of 8-byte writes would be merged into one
+// instruction whose target the compiler's copy tracking cannot place; it
+// would wait for every copy in flight.)
+template <class C>
+__device__ __forceinline__ void rows_to_slab_pair(const f32x16 (&acc)[C::FM][C::FN], const Epi& ep,
+                                              int wm, int wn, int frow, int khalf, uint16_t* x0,
+                                              uint16_t* x1) {
+    static_assert(C::BN == 128 && C::BK == 64 && C::FN == 2, "one 32-column block per slab and wave");
+    auto half = [&](const f32x16& a, int g) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ep.post * (ep.coef_acc * a[4 * g + e]);
+        return __builtin_bit_cast(uint2, __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4));
+    };
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+        const int row = wm * C::TM + i * 32 + frow;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+            uint16_t* const xs = j ? x1 : x0;
+#pragma unroll
+            for (int g = 0; g < 4; g += 2) {
+                const uint2 x = half(acc[i][j], g), y = half(acc[i][j], g + 1);
+                const auto sx = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+                const auto sy = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+                const int lch = 4 * wn + g + khalf;  // chunk of columns 8 lch .. + 7 within the slab
+                *reinterpret_cast<uint4*>(xs + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3)) =
+                    make_uint4(sx[0], sy[0], sx[1], sy[1]);
+            }
+        }
+    }
+}
+
+// Second half: as read_slab_rows, from two arrays.
+template <class C>
+__device__ __forceinline__ void read_slab_pair(const uint16_t* x0, const uint16_t* x1, SlabRows<C>& r) {
+    static_assert(C::NT == 256 && C::BM == 128, "8 chunks per thread cover the 128 x 128 tile");
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int row = 32 * (q >> 1) + (t >> 3), lch = t & 7;
+        const uint16_t* xs = (q & 1) ? x1 : x0;
+        r.v[q] = *reinterpret_cast<const uint4*>(xs + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3));
+    }
+}
+// The small class's update in strips when the class runs alone in a call:
+// the same work as ns_update_strip_kernel (B formed in the strip, the next
+// Gram's part, the tile's values stored from LDS as whole lines), but one
+// workgroup per compute unit, with twice the tiles per strip, streams its
+// tiles: the X blocks go through three LDS stages, so the copies of the next
+// two blocks are in flight while a tile is multiplied, written out and
+// (NEXT_GRAM) multiplied into the Gram part.  With half the strips, the
+// class's K-split Gram has half the parts to write and reduce.  (Beside a
+// large class on the other stream, two workgroups per compute unit share
+// the chip better: ns_update_strip_kernel.)
+//
+// The tile's values go into the X slabs its block has vacated and are
+// stored at the start of the next tile, after the wait for that tile's X
+// block (which then never has to cover them).  The stage takes the block
+// three tiles on once the tile's values have been read out.
+//
+// NEXT_GRAM: as in ns_update_strip_kernel, the planner makes the part count
+// of the class's K-split Gram equal the strip count per matrix.
+//
+// LDS (128 KB) in eight arrays of 16 KB, each a copy target of its own:
+// A's (then B's) two slabs and three stages of the X block's two k-major
+// slabs (k 0..63, 64..127; later the tile's two 64-column row slabs).  The
+// compiler tracks copies into LDS per array, for at most eight arrays, and
+// places its own waits before LDS accesses by the copies that may still be
+// in flight on any path it can see.  So every access names its array, the
+// tile loop is unrolled over the three stages, and its body has no
+// conditional copy or store: the first tile and the last few are issued
+// apart, with their conditions.
+template <class C, bool NEXT_GRAM>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void ns_update_stream_kernel(
+    const MatDesc* __restrict__ descs, int n, const int32_t* __restrict__ prefix, XcdSplit xs, int it,
+    int strip, float ca, float cb, float cc) {
+    static_assert(C::BM == 128 && C::BN == 128 && C::BK == 64 && C::NT == 256,
+                  "two 64-deep slabs hold the whole K of 128");
+    static_assert(C::RB * C::BN * 4 <= C::BK * C::BN * 2, "the Gram band fits one slab");
+    __shared__ __attribute__((aligned(1024))) uint16_t lp0[C::BM * C::BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t lp1[C::BM * C::BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t la0[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t la1[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t lb0[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t lb1[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t lc0[C::BK * C::BN];
+    __shared__ __attribute__((aligned(1024))) uint16_t lc1[C::BK * C::BN];
+    int task, q;
+    if (!xcd_task(xs, task, q)) return;  // no quarter tasks
+    const int mi = find_matrix(prefix, n, task);
+    const MatDesc& d = descs[mi];
+    const int64_t mp = d.mp, np = d.np;  // mp == 128
+    const int tiles = (int)(np / C::BN);
+    const int part = task - prefix[mi];
+    const int j0 = part * strip;
+    const int j1 = min(j0 + strip, tiles);
+    const uint16_t* A = reinterpret_cast<const uint16_t*>(d.a);
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(d.x[it & 1]);
+    Epi ep;
+    ep.outF = nullptr;
+    ep.out = reinterpret_cast<uint16_t*>(d.x[(it + 1) & 1]);
+    ep.ld_out = np;
+    ep.outT = nullptr;
+    ep.ld_outT = 0;
+    ep.E = nullptr;
+    ep.ld_e = 0;
+    ep.coef_e = 0.f;
+    ep.coef_acc = 1.f;
+    ep.post = (it == 0) ? gld(d.inv_norm) : 1.f;
+    ep.diag = 0.f;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // the wave's place in the 2 x 2 grid; its product columns are the
+    // blocks 64 jj + 32 wn .. + 31 (jj = 0, 1), one in each 64-column slab
+    const int wm = wave / C::WN, wn = wave % C::WN;
+    const int frow = lane & 31;
+    const int khalf = lane >> 5;
+    constexpr int KS = C::BK / 16;
+    f32x16 acc[C::FM][C::FN];
+    f32x16 accg[C::FM][C::FN];
+    auto zero = [](f32x16(&t)[C::FM][C::FN]) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) t[i][jj][r] = 0.f;
+    };
+    // fragments of k-step kk: rows of sp against rows of sq, or (QKN)
+    // against the k-major X slab sq.  SPLIT: the wave's column blocks one per
+    // slab (the products written to LDS: B and the tile); else the usual 64
+    // contiguous columns (the Gram part, stored by epilogue_bands)
+    auto frags = [&](const uint16_t* sp, const uint16_t* sq, int kk, bool qkn, bool split, Frags<C>& f) {
+        const int lch = 2 * kk + khalf;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) f.a[i] = read_frag<C>(sp, wm * C::TM + i * 32 + frow, lch);
+#pragma unroll
+        for (int jj = 0; jj < C::FN; ++jj) {
+            const int c0 = split ? 64 * jj + 32 * wn : wn * C::TN + jj * 32;
+            f.b[jj] = qkn ? read_frag_kn<C>(sq, 16 * kk, c0, lane) : read_frag<C>(sq, c0 + frow, lch);
+        }
+    };
+    // the products over both slabs (K = 128), software-pipelined: while the
+    // MFMAs of one k-step run, the fragments of the next are read into the
+    // other register buffer (one wave per SIMD: no other wave hides the LDS
+    // latency).  ROWS: the products held in rows (mfma_frags_rows).
+    auto product = [&](auto rows, const uint16_t* p0, const uint16_t* p1, const uint16_t* q0,
+                       const uint16_t* q1, auto qkn, bool split, f32x16(&a)[C::FM][C::FN])
+                       __attribute__((always_inline)) {
+        constexpr bool QK = decltype(qkn)::value;
+        Frags<C> f[2];
+        frags(p0, q0, 0, QK, split, f[0]);
+#pragma unroll
+        for (int st = 0; st < 2 * KS; ++st) {
+            if (st + 1 < 2 * KS) {
+                const int u = (st + 1) / KS, kk = (st + 1) % KS;
+                frags(u ? p1 : p0, u ? q1 : q0, kk, QK, split, f[(st + 1) & 1]);
+            }
+            if constexpr (decltype(rows)::value) mfma_frags_rows<C>(a, f[st & 1]);
+            else mfma_frags<C>(a, f[st & 1]);
+            interleave_reads_mfma<C::FM + (QK ? 2 : 1) * C::FN, C::FM * C::FN, 2>();
+        }
+    };
+    auto copy_x = [&](int j, uint16_t* s0, uint16_t* s1) {
+        load_slab_kn<C>(X + (int64_t)j * C::BN, np, s0, wave, lane);
+        load_slab_kn<C>(X + (int64_t)C::BK * np + (int64_t)j * C::BN, np, s1, wave, lane);
+    };
+    if constexpr (NEXT_GRAM) zero(accg);
+
+    // A's slabs, then the first three X blocks (a strip shorter than three
+    // tiles copies its last block again); A is waited for alone
+    constexpr int LX = 2 * ((C::BK / (64 / (C::BN / 8))) / C::NW);  // a thread's copies of one X block
+    load_slab<C, C::BM>(A, mp, lp0, wave, lane);
+    load_slab<C, C::BM>(A + C::BK, mp, lp1, wave, lane);
+    copy_x(j0, la0, la1);
+    wait_vmcnt<LX>();
+    copy_x(min(j0 + 1, j1 - 1), lb0, lb1);
+    copy_x(min(j0 + 2, j1 - 1), lc0, lc1);
+    lds_barrier();
+    // B = a I + b A + c A A (the polynomial's epilogue arithmetic), written
+    // over A in place once every wave has read A
+    {
+        zero(acc);
+        product(std::true_type{}, lp0, lp1, lp0, lp1, std::false_type{}, true, acc);
+        // The wave's column block jj is columns 32 wn .. + 31 of slab jj; a
+        // lane's four columns are half khalf of chunk 4 wn + g of its row.
+        // LDS is read and written in whole 16-byte chunks, lanes l and l + 32
+        // trading halves with v_permlane32_swap (chunk g of a pair goes
+        // through lane l, chunk g + 1 through lane l + 32): paired 8-byte
+        // accesses would be merged into one instruction, and a lane exchange
+        // through LDS (ds_bpermute) is an LDS access too; the compiler's copy
+        // tracking places neither, and would wait for the X copies in flight.
+        auto swap2 = [](uint2 p, uint2 q, uint2& p2, uint2& q2) {
+            const auto sx = __builtin_amdgcn_permlane32_swap(p.x, q.x, false, false);
+            const auto sy = __builtin_amdgcn_permlane32_swap(p.y, q.y, false, false);
+            p2 = make_uint2(sx[0], sy[0]);
+            q2 = make_uint2(sx[1], sy[1]);
+        };
+        uint2 e[C::FM][C::FN][4];
+        // slab by slab, each from its own array
+        auto read_a = [&](const uint16_t* ps, uint2 (&es)[C::FM][4]) {
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+                for (int gp = 0; gp < 4; gp += 2) {
+                    const int row = wm * C::TM + i * 32 + frow;
+                    const int ck = 4 * wn + gp + khalf;
+                    const uint4 r = *reinterpret_cast<const uint4*>(ps + row * C::BK + ((ck ^ swz<C::BK>(row)) << 3));
+                    // lane l: half 0 of chunks gp (its own) and gp + 1 (lane
+                    // l + 32's); lane l + 32: half 1 of both
+                    swap2(make_uint2(r.x, r.y), make_uint2(r.z, r.w), es[i][gp], es[i][gp + 1]);
+                }
+        };
+        uint2 e0[C::FM][4], e1[C::FM][4];
+        read_a(lp0, e0);
+        read_a(lp1, e1);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                e[i][0][g] = e0[i][g];
+                e[i][1][g] = e1[i][g];
+            }
+        lds_barrier();  // every wave has read A
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < C::FN; ++jj) {
+                uint16_t* const ps = jj ? lp1 : lp0;
+                const int row = wm * C::TM + i * 32 + frow;
+                uint2 o[4];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = 64 * jj + 32 * wn + 8 * g + 4 * khalf;
+                    const uint32_t w[2] = {e[i][jj][g].x, e[i][jj][g].y};
+                    float v[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t h = w[t >> 1];
+                        const float av = __builtin_bit_cast(float, (t & 1) ? (h & 0xffff0000u) : (h << 16));
+                        v[t] = 1.f * (cc * acc[i][jj][4 * g + t] + cb * av);
+                        if (row == col + t) v[t] += ca;
+                    }
+                    o[g] = __builtin_bit_cast(uint2, __builtin_convertvector(f32x4{v[0], v[1], v[2], v[3]}, bf16x4));
+                }
+#pragma unroll
+                for (int gp = 0; gp < 4; gp += 2) {
+                    const int ck = 4 * wn + gp + khalf;
+                    uint2 lo, hi;
+                    swap2(o[gp], o[gp + 1], lo, hi);
+                    *reinterpret_cast<uint4*>(ps + row * C::BK + ((ck ^ swz<C::BK>(row)) << 3)) =
+                        make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+            }
+    }
+
+    // One tile: its X block is in stage (s0, s1).  Copies of up to two
+    // later blocks stay in flight across the wait: loads land in the order
+    // issued, so once no more than AHEAD blocks' copies are outstanding, this
+    // block's have landed, and every store issued since only makes the count
+    // smaller.  FIRST: the strip's first tile (nothing to store yet).  COPY:
+    // at the end the tile's stage takes block `next`.
+    // Every count and condition is fixed per call site, except in the
+    // strip's first tile: the compiler places its own waits by the copies in
+    // flight on every path it can see, and a copy that it cannot prove
+    // issued would cost a full wait in the tiles after it.
+    SlabRows<C> out;
+    auto tile = [&](auto ahead, auto first, auto copy, int j, int next, uint16_t* s0, uint16_t* s1)
+                    __attribute__((always_inline)) {
+        constexpr int AH = decltype(ahead)::value;
+        if constexpr (AH >= 2) wait_vmcnt<2 * LX>();
+        else if constexpr (AH == 1) wait_vmcnt<LX>();
+        else if constexpr (AH == 0) wait_vmcnt<0>();
+        else {  // the first tile: blocks j0 + 1 and j0 + 2 are copied if they exist
+            const int ah = min(2, j1 - 1 - j);
+            if (ah >= 2) wait_vmcnt<2 * LX>();
+            else if (ah == 1) wait_vmcnt<LX>();
+            else wait_vmcnt<0>();
+        }
+        lds_barrier();  // X(j) in every wave; B written; the last tile's values read
+        if constexpr (!decltype(first)::value) store_slab_rows<C>(out, (int64_t)(j - 1) * C::BN, ep);
+        zero(acc);
+        product(std::true_type{}, lp0, lp1, s0, s1, std::true_type{}, true, acc);
+        lds_barrier();  // every wave is done with X(j)
+        rows_to_slab_pair<C>(acc, ep, wm, wn, frow, khalf, s0, s1);
+        lds_barrier();
+        read_slab_pair<C>(s0, s1, out);
+        if constexpr (NEXT_GRAM) product(std::false_type{}, s0, s1, s0, s1, std::false_type{}, false, accg);
+        lds_barrier();  // the tile's values are read: the stage takes the next block
+        if constexpr (decltype(copy)::value) copy_x(next, s0, s1);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    using Run = std::integral_constant<int, -1>;
+    // The first tile (stage a) copies block j0 + 3 into its stage, or the
+    // strip's last block again when there is none (never read), so that the
+    // same copies are in flight whatever the strip's length.  Then whole
+    // rounds of the stages b, c, a while the blocks three tiles on exist, and
+    // the R <= 5 tiles left, each count fixed (tail<R>).
+    using Two = std::integral_constant<int, 2>;
+    tile(Run{}, T_{}, T_{}, j0, min(j0 + 3, j1 - 1), la0, la1);
+    int j = j0 + 1;
+    for (; j + 5 < j1; j += 3) {
+        tile(Two{}, F_{}, T_{}, j, j + 3, lb0, lb1);
+        tile(Two{}, F_{}, T_{}, j + 1, j + 4, lc0, lc1);
+        tile(Two{}, F_{}, T_{}, j + 2, j + 5, la0, la1);
+    }
+    auto tail = [&](auto r) __attribute__((always_inline)) {
+        constexpr int R = decltype(r)::value;
+        // tile t of the tail is block j + t in stage b, c, a, b, c; it copies
+        // block j + t + 3 when that exists, and waits for its own block with
+        // min(2, R - 1 - t) later blocks in flight
+        using A0 = std::integral_constant<int, (R - 1 < 2 ? R - 1 : 2)>;
+        using A1 = std::integral_constant<int, (R - 2 < 2 ? R - 2 : 2)>;
+        using A2 = std::integral_constant<int, (R - 3 < 2 ? R - 3 : 2)>;
+        using A3 = std::integral_constant<int, (R - 4 < 2 ? R - 4 : 2)>;
+        if constexpr (R > 0) tile(A0{}, F_{}, std::bool_constant<(R > 3)>{}, j, j + 3, lb0, lb1);
+        if constexpr (R > 1) tile(A1{}, F_{}, std::bool_constant<(R > 4)>{}, j + 1, j + 4, lc0, lc1);
+        if constexpr (R > 2) tile(A2{}, F_{}, F_{}, j + 2, 0, la0, la1);
+        if constexpr (R > 3) tile(A3{}, F_{}, F_{}, j + 3, 0, lb0, lb1);
+        if constexpr (R > 4) tile(std::integral_constant<int, 0>{}, F_{}, F_{}, j + 4, 0, lc0, lc1);
+    };
+    switch (j1 - j) {
+        case 1: tail(std::integral_constant<int, 1>{}); break;
+        case 2: tail(std::integral_constant<int, 2>{}); break;
+        case 3: tail(std::integral_constant<int, 3>{}); break;
+        case 4: tail(std::integral_constant<int, 4>{}); break;
+        case 5: tail(std::integral_constant<int, 5>{}); break;
+        default: break;  // none left
+    }
+    store_slab_rows<C>(out, (int64_t)(j1 - 1) * C::BN, ep);
+    if constexpr (NEXT_GRAM) {
+        // this strip's part of the next Gram: raw fp32, as the K-split Gram
+        // stores it, through the first stage's first slab (every copy has
+        // landed; the band loop's first barrier follows the last reads)
+        Epi eg;
+        eg.outF = d.gram_part + (int64_t)part * C::BM * C::BN;
+        eg.out = nullptr;
+        eg.ld_out = 0;
+        eg.outT = nullptr;
+        eg.ld_outT = 0;
+        eg.E = nullptr;
+        eg.ld_e = 0;
+        eg.coef_e = 0.f;
+        eg.coef_acc = 1.f;
+        eg.post = 1.f;
+        eg.diag = 0.f;
+        epilogue_bands<C, false, true, true>(accg, 0, 0, eg, reinterpret_cast<float*>(la0), wm, wn, frow,
+                                             khalf);
+    }
+}
+
 // ---- fp32 operands: the full-precision option on the matrix cores ---------
 //
 // The fp32 class's three products (X and X^T kept side by side, 64-padded;
@@ -1667,8 +2031,17 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 }
 
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
-                                   const XcdSplit& xs, int it, int strip, int next_gram, float a, float b,
-                                   float c, hipStream_t st) {
+                                   const XcdSplit& xs, int it, int strip, int next_gram, int stream,
+                                   float a, float b, float c, hipStream_t st) {
+    if (stream) {
+        if (next_gram)
+            ns_update_stream_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip,
+                                                                                       xs, it, strip, a, b, c);
+        else
+            ns_update_stream_kernel<SmallCfg, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
+                d, n, prefix_strip, xs, it, strip, a, b, c);
+        return hipGetLastError();
+    }
     if (next_gram)
         ns_update_strip_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs,
                                                                                       it, strip, a, b, c);

@@ -98,10 +98,12 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 // workgroup; prefix_strip: strips per matrix, prefix-summed.  Each strip
 // forms B = a I + b A + c A A from A itself (no polynomial launch for the
 // class).  next_gram: each strip also stores its part of the next
-// iteration's K-split Gram (the strip count per matrix equals its gram_split)
+// iteration's K-split Gram (the strip count per matrix equals its gram_split).
+// stream: one workgroup per compute unit streaming its tiles (the class runs
+// alone in the call), else two per compute unit
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
-                                   const XcdSplit& xs, int it, int strip, int next_gram, float a, float b,
-                                   float c, hipStream_t st);
+                                   const XcdSplit& xs, int it, int strip, int next_gram, int stream,
+                                   float a, float b, float c, hipStream_t st);
 
 // fp32 class (p.gram == p.tri: the prefix counts every tile of the square).
 // kmax: the largest K of the launch's matrices (n' for the Gram, m' for the

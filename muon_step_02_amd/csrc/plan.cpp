@@ -342,6 +342,52 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         // compute slots: two 128-tile workgroups fit one compute unit's LDS
         const int slots = 8 * cus * (c == kSmall ? 2 : 1);
         if (c != kF32 && C.count > 0) S = gram_splits(tg, slabs, slots);
+        // The small class's update in strips: as many consecutive column
+        // tiles per workgroup as it takes to fill the compute units once,
+        // when that is at least two (one tile per workgroup runs the copy
+        // latency and the epilogue back to back).  Alone in the call, the
+        // class streams its strips at one workgroup per compute unit, and a
+        // K-split Gram takes as many parts per matrix as the matrix has
+        // strips (at most kMaxSplit, each of at least kMinSplitSlabs slabs),
+        // so that from the second iteration on
+        // the update's strips form the parts.  Beside another class (on the
+        // other stream) it runs two workgroups per compute unit, and the
+        // strips form the Gram parts when their count per matrix already
+        // equals the split's.
+        C.strip = 0;
+        C.stream = false;
+        C.fuse_gram = false;
+        C.pstrip.assign(C.count + 1, 0);
+        std::vector<int32_t> ts;
+        if (c == kSmall && C.count > 0) {
+            const bool alone = P.cls[kLarge].count == 0 && P.cls[kF32].count == 0;
+            const int64_t wgs = (alone ? 8 : 16) * (int64_t)cus;
+            int64_t upd = 0;
+            for (int k = 0; k < C.count; ++k) upd += tu[k];
+            const int64_t L = (upd + wgs - 1) / wgs;
+            if (L >= 2) {
+                C.strip = (int)L;
+                C.stream = alone;
+                ts.resize(C.count);
+                bool split = false, several = false, fits = true, same = true;
+                for (int k = 0; k < C.count; ++k) {
+                    ts[k] = (int32_t)((tu[k] + L - 1) / L);
+                    C.pstrip[k + 1] = C.pstrip[k] + ts[k];
+                    split = split || S[k] > 1;
+                    several = several || ts[k] > 1;
+                    fits = fits && ts[k] <= kMaxSplit && (int64_t)ts[k] * kMinSplitSlabs <= slabs[k];
+                    same = same && ts[k] == S[k];
+                }
+                C.total_strips = C.pstrip[C.count];
+                if (alone) {
+                    C.fuse_gram = split && several && fits;
+                    if (C.fuse_gram)
+                        for (int k = 0; k < C.count; ++k) S[k] = ts[k];
+                } else {
+                    C.fuse_gram = split && same;
+                }
+            }
+        }
         int64_t tasks = 0;
         for (int k = 0; k < C.count; ++k) {
             P.d[C.first + k].gram_split = S[k];
@@ -395,30 +441,9 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         C.xs_gram = xcd_split(tk.data(), wn.data(), C.count, cus, C.gram_split ? 0 : quarters, 1);
         C.xs_poly = xcd_split(tp.data(), wm.data(), C.count, cus, C.poly_small ? 0 : quarters, 0);
         C.xs_upd = xcd_split(tu.data(), wm.data(), C.count, cus, quarters, 1);
-        // The small class's update in strips: as many consecutive column
-        // tiles per workgroup as it takes to fill two workgroups per compute
-        // unit once, when that is at least two (one tile per workgroup runs
-        // the copy latency and the epilogue back to back).
-        C.strip = 0;
-        C.pstrip.assign(C.count + 1, 0);
-        if (c == kSmall) {
-            const int64_t slots = 2 * 8 * (int64_t)cus;
-            const int64_t L = ((int64_t)C.total_upd + slots - 1) / slots;
-            if (L >= 2) {
-                C.strip = (int)L;
-                std::vector<int32_t> ts(C.count);
-                std::vector<int64_t> wsz(C.count, L);
-                for (int k = 0; k < C.count; ++k) {
-                    ts[k] = (int32_t)((tu[k] + L - 1) / L);
-                    C.pstrip[k + 1] = C.pstrip[k] + ts[k];
-                }
-                C.total_strips = C.pstrip[C.count];
-                C.xs_strip = xcd_split(ts.data(), wsz.data(), C.count, cus, 0, 0);
-                bool fuse = C.gram_split;
-                for (int k = 0; k < C.count && fuse; ++k)
-                    fuse = ts[k] == P.d[C.first + k].gram_split;
-                C.fuse_gram = fuse;
-            }
+        if (C.strip > 0) {
+            std::vector<int64_t> wsz(C.count, C.strip);
+            C.xs_strip = xcd_split(ts.data(), wsz.data(), C.count, cus, 0, 0);
         }
     }
 

@@ -33,6 +33,10 @@ struct ClassPlan {
     // Gram parts: from the second iteration on, the update's strips store the
     // Gram parts and the split Gram launch is skipped
     bool fuse_gram = false;
+    // small class alone in the call: strips for one workgroup per compute
+    // unit, streamed (and a K-split Gram cut into as many parts as strips);
+    // else strips for two workgroups per compute unit
+    bool stream = false;
     int kmax_n = 0, kmax_m = 0;         // largest padded n' and m' of the class
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };

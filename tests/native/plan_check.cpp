@@ -349,12 +349,15 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
         EXPECT(C.xs_gram.interleaved == 1 && C.xs_poly.interleaved == 0 && C.xs_upd.interleaved == 1);
         check_split(C.xs_poly, C.total_poly, cus, c == kLarge && !C.poly_small);
         // the small class's update in strips exactly when two or more tiles per
-        // workgroup fill two workgroups per compute unit once; strips cover
-        // each matrix's column tiles once, in order
+        // workgroup fill the compute units once (one workgroup each, streamed,
+        // when the class is alone in the call, else two); strips cover each
+        // matrix's column tiles once, in order
         if (c == kSmall) {
-            const int64_t slots = 16 * (int64_t)cus;
+            const bool alone = P.cls[kLarge].count == 0 && P.cls[kF32].count == 0;
+            const int64_t slots = (alone ? 8 : 16) * (int64_t)cus;
             const int64_t L = (C.total_upd + slots - 1) / slots;
             EXPECT(C.strip == (L >= 2 ? (int)L : 0));
+            EXPECT(C.stream == (C.strip > 0 && alone));
             if (C.strip > 0) {
                 int64_t run = 0;
                 EXPECT(C.pstrip.size() == (size_t)C.count + 1 && C.pstrip[0] == 0);
@@ -377,7 +380,7 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
                 EXPECT(memcmp(img.data() + C.off_pstrip, C.pstrip.data(), 4 * (size_t)(C.count + 1)) == 0);
             }
         } else {
-            EXPECT(C.strip == 0 && !C.fuse_gram);
+            EXPECT(C.strip == 0 && !C.fuse_gram && !C.stream);
         }
         check_split(C.xs_upd, C.total_upd, cus, c == kLarge);
     }
@@ -511,22 +514,42 @@ int main(int argc, char** argv) {
         // 105 tiles of 256 (3584^2) would be 420 quarter slots; 406 tiles of 128 fit one round
         plan_of({{3584, 3584}}, P);
         EXPECT(P.cls[kLarge].poly_small && P.cls[kLarge].total_poly == 406);
-        // per head: 64 blocks of 128 x 7168 (56 column tiles each) in strips of 7
+        // per head alone: 64 blocks of 128 x 7168 (56 column tiles each) in
+        // streamed strips of 14, the K-split Gram in as many parts (4)
         plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 7168}), P);
-        EXPECT(P.cls[kSmall].strip == 7 && P.cls[kSmall].total_strips == 512);
-        EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram && P.d[0].gram_split == 8);
-        // 16 blocks of 100 x 4900 (39 tiles each): strips of 2, the last one short
+        EXPECT(P.cls[kSmall].strip == 14 && P.cls[kSmall].total_strips == 256 && P.cls[kSmall].stream);
+        EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram && P.d[0].gram_split == 4);
+        // the same blocks beside a 4096^2 matrix: strips of 7 for two
+        // workgroups per compute unit, 8 Gram parts, not streamed
+        {
+            std::vector<std::pair<int64_t, int64_t>> sh(64, {128, 7168});
+            sh.push_back({4096, 4096});
+            plan_of(sh, P);
+            EXPECT(P.cls[kSmall].strip == 7 && P.cls[kSmall].total_strips == 512 && !P.cls[kSmall].stream);
+            EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram);
+            EXPECT(P.d[P.cls[kSmall].first].gram_split == 8);
+        }
+        // 16 blocks of 100 x 4900 (39 tiles, 78 slabs each), alone: streamed
+        // strips of 3, 13 per block; 13 Gram parts would be shorter than
+        // kMinSplitSlabs, so the Gram keeps its own 9 parts and no fusion
         plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
-        EXPECT(P.cls[kSmall].strip == 2 && P.cls[kSmall].total_strips == 16 * 20);
+        EXPECT(P.cls[kSmall].strip == 3 && P.cls[kSmall].total_strips == 16 * 13 && P.cls[kSmall].stream);
+        EXPECT(P.cls[kSmall].gram_split && !P.cls[kSmall].fuse_gram && P.d[0].gram_split == 9);
         // few small tiles: one tile per workgroup
         plan_of({{128, 4096}, {100, 3000}}, P);
-        EXPECT(P.cls[kSmall].strip == 0 && !P.cls[kSmall].fuse_gram);
-        // 64 heads of 128 x 3584: 7 Gram parts of 8 slabs and 7 strips of 4 tiles
+        EXPECT(P.cls[kSmall].strip == 0 && !P.cls[kSmall].fuse_gram && !P.cls[kSmall].stream);
+        // 64 heads of 128 x 3584 alone: strips of 7 (4 per head), 4 Gram parts
         plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 3584}), P);
-        EXPECT(P.cls[kSmall].strip == 4 && P.d[0].gram_split == 7 && P.cls[kSmall].fuse_gram);
-        // strips of 2 against 9 Gram parts: no fusion
-        plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
-        EXPECT(P.cls[kSmall].gram_split && !P.cls[kSmall].fuse_gram);
+        EXPECT(P.cls[kSmall].strip == 7 && P.d[0].gram_split == 4 && P.cls[kSmall].fuse_gram);
+        // beside a large matrix, 16 blocks of 100 x 4900: strips of 2 against
+        // 9 Gram parts, no fusion
+        {
+            std::vector<std::pair<int64_t, int64_t>> sh(16, {100, 4900});
+            sh.push_back({1024, 1024});
+            plan_of(sh, P);
+            EXPECT(P.cls[kSmall].strip == 2 && !P.cls[kSmall].stream);
+            EXPECT(P.cls[kSmall].gram_split && !P.cls[kSmall].fuse_gram);
+        }
     }
     // xcd_split on its own: degenerate inputs
     {

@@ -314,3 +314,40 @@ def test_per_head_column_blocks_fused_strips():
                                                        TOL_O_BF16), h
     last = slice((heads - 1) * dh, heads * dh)
     assert torch.equal(Wf[:, last], W0f[:, last]) and torch.count_nonzero(Mf[:, last]) == 0
+
+
+@pytest.mark.parametrize("tiles,tall", [(5, False), (10, True), (23, False), (31, False)],
+                         ids=["strips 2-2-1", "tall, strips 3-3-3-1", "strips 6-6-6-5, fused",
+                              "strips 8-8-8-7, fused"])
+def test_small_class_alone_streamed_strips(tiles, tall):
+    # 64 blocks of 128 x 128*tiles (or their transposes), the small class alone
+    # in the call: its update streams strips of ceil(tiles / 4) column tiles at
+    # one workgroup per compute unit, the last strip of every block shorter.
+    # The strip lengths reach every tail length of the streaming kernel's loop
+    # (first tile, whole rounds of three, then 0-5 tiles); with parts of at
+    # least 8 slabs the K-split Gram takes one part per strip and the strips
+    # form the next Gram's parts (fused), else the Gram runs split each
+    # iteration.  Sampled blocks against the oracle over two carried steps.
+    from harness import TOL_BLOCK_BF16, check_output
+    blocks, dh = 64, 128
+    dm = 128 * tiles
+    shape = (dm, dh) if tall else (dh, dm)
+    Ws = [_weight(*shape, 300 + i) for i in range(blocks)]
+    Ms = [torch.zeros(*shape, device=DEV) for _ in range(blocks)]
+    Os = [torch.empty(*shape, device=DEV) for _ in range(blocks)]
+    sample = [0, 1, 17, 31, 32, 50, 62, 63]
+    ref = {b: [f64(Ws[b]), np.zeros(shape)] for b in sample}
+    kw = oracle_kwargs(BASE_HP)
+    for step in range(2):
+        Gs = [_grad(*shape, 400 + 100 * step + i) for i in range(blocks)]
+        run_muon_step([mu.muon_matrix(Ws[i], Gs[i], Ms[i], update_out=Os[i]) for i in range(blocks)],
+                      hp_from(BASE_HP))
+        torch.cuda.synchronize()
+        for b in sample:
+            W0, M0 = ref[b]
+            Wr, Mr, Or = oracle.muon_matrix_step(W0, f64(Gs[b]), M0, **kw)
+            check_output(f64(Os[b]), Or, TOL_O_BF16, TOL_BLOCK_BF16, what="block %d step %d" % (b, step))
+            assert relF(f64(Ms[b]), Mr) <= TOL_STATE, (step, b)
+            assert relF(f64(Ws[b]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(*shape), Or, Wr,
+                                                       TOL_O_BF16), (step, b)
+            ref[b] = [f64(Ws[b]), f64(Ms[b])]
