@@ -1497,6 +1497,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         case 5: tail(std::integral_constant<int, 5>{}); break;
         default: break;  // none left
     }
+    // every copy has landed (a strip's first tile always copies, for a strip
+    // of one tile its own block again) before the band buffer reuses the
+    // first stage and before the workgroup ends
+    wait_vmcnt<0>();
     store_slab_rows<C>(out, (int64_t)(j1 - 1) * C::BN, ep);
     if constexpr (NEXT_GRAM) {
         // this strip's part of the next Gram: raw fp32, as the K-split Gram

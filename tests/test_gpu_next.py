@@ -316,26 +316,28 @@ def test_per_head_column_blocks_fused_strips():
     assert torch.equal(Wf[:, last], W0f[:, last]) and torch.count_nonzero(Mf[:, last]) == 0
 
 
-@pytest.mark.parametrize("tiles,tall", [(5, False), (10, True), (23, False), (31, False)],
+@pytest.mark.parametrize("blocks,tiles,tall", [(64, 5, False), (64, 10, True), (64, 23, False), (64, 31, False),
+                                               (32, 36, False)],
                          ids=["strips 2-2-1", "tall, strips 3-3-3-1", "strips 6-6-6-5, fused",
-                              "strips 8-8-8-7, fused"])
-def test_small_class_alone_streamed_strips(tiles, tall):
-    # 64 blocks of 128 x 128*tiles (or their transposes), the small class alone
-    # in the call: its update streams strips of ceil(tiles / 4) column tiles at
-    # one workgroup per compute unit, the last strip of every block shorter.
+                              "strips 8-8-8-7, fused", "strips 5 x 7 + 1, fused"])
+def test_small_class_alone_streamed_strips(blocks, tiles, tall):
+    # `blocks` blocks of 128 x 128*tiles (or their transposes), the small class
+    # alone in the call: its update streams strips of ceil(blocks * tiles / 256)
+    # column tiles at one workgroup per compute unit, the last strip of every
+    # block shorter (down to one tile, whose strip copies its block twice).
     # The strip lengths reach every tail length of the streaming kernel's loop
     # (first tile, whole rounds of three, then 0-5 tiles); with parts of at
     # least 8 slabs the K-split Gram takes one part per strip and the strips
     # form the next Gram's parts (fused), else the Gram runs split each
     # iteration.  Sampled blocks against the oracle over two carried steps.
     from harness import TOL_BLOCK_BF16, check_output
-    blocks, dh = 64, 128
+    dh = 128
     dm = 128 * tiles
     shape = (dm, dh) if tall else (dh, dm)
     Ws = [_weight(*shape, 300 + i) for i in range(blocks)]
     Ms = [torch.zeros(*shape, device=DEV) for _ in range(blocks)]
     Os = [torch.empty(*shape, device=DEV) for _ in range(blocks)]
-    sample = [0, 1, 17, 31, 32, 50, 62, 63]
+    sample = sorted({0, 1, 17, blocks // 2 - 1, blocks // 2, blocks - 2, blocks - 1})
     ref = {b: [f64(Ws[b]), np.zeros(shape)] for b in sample}
     kw = oracle_kwargs(BASE_HP)
     for step in range(2):
