@@ -353,3 +353,22 @@ def test_small_class_alone_streamed_strips(blocks, tiles, tall):
             assert relF(f64(Ws[b]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(*shape), Or, Wr,
                                                        TOL_O_BF16), (step, b)
             ref[b] = [f64(Ws[b]), f64(Ms[b])]
+
+
+def test_streamed_strips_with_fused_gram_parts_are_repeatable():
+    # The streamed strips form the next Gram's parts and the reduce sums them
+    # in part order, so two runs from the same state give the same bits
+    # (64 blocks of 128 x 2944: strips of 6 tiles, 4 parts per block).
+    blocks, shape = 64, (128, 128 * 23)
+    res = []
+    for _ in range(2):
+        Ws = [_weight(*shape, 700 + i) for i in range(blocks)]
+        Gs = [_grad(*shape, 800 + i) for i in range(blocks)]
+        Ms = [torch.zeros(*shape, device=DEV) for _ in range(blocks)]
+        Os = [torch.empty(*shape, device=DEV) for _ in range(blocks)]
+        run_muon_step([mu.muon_matrix(Ws[i], Gs[i], Ms[i], update_out=Os[i]) for i in range(blocks)],
+                      hp_from(BASE_HP))
+        torch.cuda.synchronize()
+        res.append([t.clone() for t in Ws + Ms + Os])
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
