@@ -16,16 +16,22 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 
-# mixed shapes: square, wide, tall (transposed), and a small-class block
-SHAPES = [(512, 384), (256, 768), (1024, 640), (128, 512)]
+SHAPE_SETS = {
+    # mixed shapes: square, wide, tall (transposed), and a small-class block
+    "mixed": [(512, 384), (256, 768), (1024, 640), (128, 512)],
+    # 64 blocks of 128 x 2944, the small class alone: its update streams strips
+    # of 6 column tiles that also form the next iteration's 4 Gram parts per
+    # block, summed by the reduce launch
+    "small class alone, streamed strips": [(128, 128 * 23)] * 64,
+}
 ADAMW_SHAPES = [(1000,), (64, 33)]
 
 
-def _state(seed):
+def _state(seed, shapes):
     g = torch.Generator(device=DEV).manual_seed(seed)
-    W = [torch.randn(s, generator=g, device=DEV) * 0.02 for s in SHAPES]
-    G = [torch.randn(s, generator=g, device=DEV) for s in SHAPES]
-    M = [torch.zeros(s, device=DEV) for s in SHAPES]
+    W = [torch.randn(s, generator=g, device=DEV) * 0.02 for s in shapes]
+    G = [torch.randn(s, generator=g, device=DEV) for s in shapes]
+    M = [torch.zeros(s, device=DEV) for s in shapes]
     P = [torch.randn(s, generator=g, device=DEV) for s in ADAMW_SHAPES]
     Q = [torch.randn(s, generator=g, device=DEV) * 3.0 for s in ADAMW_SHAPES]
     m = [torch.zeros(s, device=DEV) for s in ADAMW_SHAPES]
@@ -54,9 +60,10 @@ class Step:
         mu.adamw_step_clipped(self.h, self.ts, self.ahp, 1.0, self.aws, norm_out=self.norm)
 
 
-def test_graph_replays_equal_eager_steps():
+@pytest.mark.parametrize("shapes", list(SHAPE_SETS.values()), ids=list(SHAPE_SETS))
+def test_graph_replays_equal_eager_steps(shapes):
     h = Handle.get()
-    eager_state, graph_state = _state(11), _state(11)
+    eager_state, graph_state = _state(11, shapes), _state(11, shapes)
     eager, captured = Step(h, eager_state), Step(h, graph_state)
     torch.cuda.synchronize()
 
