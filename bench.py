@@ -239,7 +239,16 @@ def main():
     ew_bytes = {"momentum": ((g_bytes + 4 + 4 + ns_b) * el, (g_bytes + 4 + 4 + ns_copies * ns_b) * el),
                 "apply": ((4 + ns_b + 4) * el, (4 + ns_b + 4) * el)}
     hbm = {}
+    # A small class alone whose weights are plain fp32 blocks applies the step
+    # inside its last update (no apply launch): that launch reads and writes W
+    # (8 B per element) where it would have written X (2 B).
+    apply_fused = phases["apply"][1] == 0 and phases["update"][1] > 0
+    if apply_fused:
+        update_bytes += (8 - ns_b) * el / hpd["steps"]
     for ph, (b, b_act) in ew_bytes.items():
+        if ph == "apply" and apply_fused:
+            hbm[ph] = {"fused_into": "update", "launches_per_step": 0}
+            continue
         # per step: every launch of the phase (one per elementwise tile kind in use)
         ms, cnt = phases[ph]
         avg = ms / max(args.steps, 1)

@@ -313,8 +313,9 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
                     return launch_update_strip_bf16(dc, C.count,
                                                     reinterpret_cast<const int32_t*>(ws + C.off_pstrip),
                                                     C.xs_strip, it, C.strip,
-                                                    C.fuse_gram && it + 1 < hp->ns_steps, C.stream, a, b,
-                                                    c, sk);
+                                                    C.fuse_gram && it + 1 < hp->ns_steps, C.stream,
+                                                    C.fuse_apply && it + 1 == hp->ns_steps, a, b, c,
+                                                    1.f - hp->lr * hp->weight_decay, hp->lr, sk);
                 return launch_update_bf16(dc, C.count, pc[k], C.xs_upd, it, k == kSmall, sk);
             });
         }
@@ -326,7 +327,8 @@ muon_status muon_step_batched(muon_handle h, const muon_matrix* mats, int n,
         if (ej == hipSuccess) ej = hipStreamWaitEvent(s, h->join, 0);
         if (e == hipSuccess) e = ej;
     }
-    if (e == hipSuccess)
+    // a class that applied in its last update is every matrix of the call
+    if (e == hipSuccess && !P.cls[kSmall].fuse_apply)
         e = timed(h, 5, s, [&] {
             return launch_apply(dd, n, eg, hp->ns_steps & 1, hp->lr, hp->weight_decay, hp->qk_tau, s);
         });

@@ -375,7 +375,9 @@ __device__ __forceinline__ void apply_tile(const MatDesc& d, int lt, int parity,
             clip = sm > qk_tau ? sqrtf(qk_tau / sm) : 1.f;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[q].v[e] = clip * (decay * w[q].v[e] - sc * o[q][e]);
+        // one explicit fma, so that the streamed update that applies the
+        // step itself rounds the same way
+        for (int e = 0; e < 4; ++e) w[q].v[e] = clip * __builtin_fmaf(decay, w[q].v[e], -(sc * o[q][e]));
         store4<VEC>(d.param, PBF, r * d.ld_param + c, w[q], valid[q]);
         if (d.update_out) {
             Vals4 ov;

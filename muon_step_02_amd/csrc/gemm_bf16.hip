@@ -1211,6 +1211,29 @@ __device__ __forceinline__ void read_slab_pair(const uint16_t* x0, const uint16_
         r.v[q] = *reinterpret_cast<const uint4*>(xs + row * C::BK + ((lch ^ swz<C::BK>(row)) << 3));
     }
 }
+// The tile's values as the streaming kernel's APPLY variant reads them:
+// chunk k of thread t is 4 columns 4 (t % 16) of slab k & 1 in row
+// 16 (k >> 1) + t / 16, so that a wave's 64 lanes cover 4 rows x 64 columns
+// and its 16-byte fp32 accesses to W whole 128-byte lines.  The offsets are
+// laundered one by one: two reads a fixed distance apart would be merged into
+// one instruction that the compiler's copy tracking cannot place.
+template <class C>
+struct SlabQuads {
+    uint2 v[16];
+};
+template <class C>
+__device__ __forceinline__ void read_slab_quads(const uint16_t* x0, const uint16_t* x1, SlabQuads<C>& r) {
+    static_assert(C::NT == 256 && C::BM == 128 && C::BK == 64, "16 chunks per thread cover the 128 x 128 tile");
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int row = 16 * (k >> 1) + (t >> 4), c4 = t & 15;
+        int off = row * C::BK + ((((c4 >> 1) ^ swz<C::BK>(row)) << 3) | ((c4 & 1) << 2));
+        asm volatile("" : "+v"(off));
+        const uint16_t* xs = (k & 1) ? x1 : x0;
+        r.v[k] = *reinterpret_cast<const uint2*>(xs + off);
+    }
+}
 // The small class's update in strips when the class runs alone in a call:
 // the same work as ns_update_strip_kernel (B formed in the strip, the next
 // Gram's part, the tile's values stored from LDS as whole lines), but one
@@ -1230,6 +1253,15 @@ __device__ __forceinline__ void read_slab_pair(const uint16_t* x0, const uint16_
 // NEXT_GRAM: as in ns_update_strip_kernel, the planner makes the part count
 // of the class's K-split Gram equal the strip count per matrix.
 //
+// APPLY (the last iteration, fp32 weights of exactly 128 x 128k, not
+// transposed, no QK-Clip, no separate update output): instead of storing X,
+// each tile updates its block of W in place, W <- decay W - lr scale X, with
+// X rounded to bf16 first, as the apply kernel does.  W goes through
+// registers: a tile's block of W is loaded at the end of the tile before,
+// ahead of that tile's copy of the X block three tiles on, and the tile
+// applies it at its own end, once its values are out of LDS; waiting for
+// those loads then leaves the next X block's copies in flight.
+//
 // LDS (128 KB) in eight arrays of 16 KB, each a copy target of its own:
 // A's (then B's) two slabs and three stages of the X block's two k-major
 // slabs (k 0..63, 64..127; later the tile's two 64-column row slabs).  The
@@ -1239,12 +1271,13 @@ __device__ __forceinline__ void read_slab_pair(const uint16_t* x0, const uint16_
 // tile loop is unrolled over the three stages, and its body has no
 // conditional copy or store: the first tile and the last few are issued
 // apart, with their conditions.
-template <class C, bool NEXT_GRAM>
+template <class C, bool NEXT_GRAM, bool APPLY>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void ns_update_stream_kernel(
     const MatDesc* __restrict__ descs, int n, const int32_t* __restrict__ prefix, XcdSplit xs, int it,
-    int strip, float ca, float cb, float cc) {
+    int strip, float ca, float cb, float cc, float decay, float lr) {
     static_assert(C::BM == 128 && C::BN == 128 && C::BK == 64 && C::NT == 256,
                   "two 64-deep slabs hold the whole K of 128");
+    static_assert(!(NEXT_GRAM && APPLY), "only the last iteration applies");
     static_assert(C::RB * C::BN * 4 <= C::BK * C::BN * 2, "the Gram band fits one slab");
     __shared__ __attribute__((aligned(1024))) uint16_t lp0[C::BM * C::BK];
     __shared__ __attribute__((aligned(1024))) uint16_t lp1[C::BM * C::BK];
@@ -1335,6 +1368,45 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         load_slab_kn<C>(X + (int64_t)C::BK * np + (int64_t)j * C::BN, np, s1, wave, lane);
     };
     if constexpr (NEXT_GRAM) zero(accg);
+    // APPLY: W's values under a thread's 16 chunks of 4 columns (SlabQuads:
+    // row 16 (k >> 1) + t / 16, columns 64 (k & 1) + 4 (t % 16)), one 16-byte
+    // buffer load each (buffer, not flat, accesses: a flat one counts as an
+    // LDS access too, and its wait would cover every copy in flight).  The
+    // planner keeps the byte offsets below 2 GB.
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(APPLY ? d.param : nullptr, 0,
+                                                                         0x7fffffff, 0x00020000);
+    const int64_t ldw = d.ld_param;
+    const float sc = lr * d.scale;
+    auto w_off = [&](int j, int k) {
+        const int t = threadIdx.x;
+        return (uint32_t)(((int64_t)(16 * (k >> 1) + (t >> 4)) * ldw + (int64_t)j * C::BN + 64 * (k & 1) +
+                           4 * (t & 15)) * 4);
+    };
+    auto load_w = [&](int j, f32x4 (&w)[16]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            w[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, w_off(j, k), 0, 2));
+    };
+    // tile j's new W from its values x and its W in w; then (LOADW) tile wj's
+    // W is loaded into w, and the new values stored
+    auto apply_w = [&](int j, const SlabQuads<C>& x, f32x4 (&w)[16], auto loadw, int wj)
+                       __attribute__((always_inline)) {
+        f32x4 o[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t b = (e >> 1) ? x.v[k].y : x.v[k].x;
+                const float xv = __builtin_bit_cast(float, (e & 1) ? (b & 0xffff0000u) : (b << 16));
+                o[k][e] = __builtin_fmaf(decay, w[k][e], -(sc * xv));
+            }
+        if constexpr (decltype(loadw)::value) load_w(wj, w);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(GWord<16>::T, o[k]), wr, w_off(j, k), 0,
+                                                   kStreamStore);
+    };
+    f32x4 wv[16];
 
     // A's slabs, then the first three X blocks (a strip shorter than three
     // tiles copies its last block again); A is waited for alone
@@ -1345,6 +1417,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     wait_vmcnt<LX>();
     copy_x(min(j0 + 1, j1 - 1), lb0, lb1);
     copy_x(min(j0 + 2, j1 - 1), lc0, lc1);
+    if constexpr (APPLY) load_w(j0, wv);
     lds_barrier();
     // B = a I + b A + c A A (the polynomial's epilogue arithmetic), written
     // over A in place once every wave has read A
@@ -1433,29 +1506,38 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     // strip's first tile: the compiler places its own waits by the copies in
     // flight on every path it can see, and a copy that it cannot prove
     // issued would cost a full wait in the tiles after it.
+    // APPLY: 16 W loads follow the prologue's copies and precede each copy
+    // at a tile's end, so a wait leaving AH blocks' copies in flight may
+    // leave WX = 16 more loads (at least 16 more than that were issued after
+    // any block a tile waits for; counting fewer only waits longer).
+    // LOADW: at its end the tile loads W of tile wj.
+    constexpr int WX = APPLY ? 16 : 0;
     SlabRows<C> out;
-    auto tile = [&](auto ahead, auto first, auto copy, int j, int next, uint16_t* s0, uint16_t* s1)
-                    __attribute__((always_inline)) {
+    SlabQuads<C> outq;
+    auto tile = [&](auto ahead, auto first, auto copy, int j, int next, uint16_t* s0, uint16_t* s1,
+                    auto loadw, int wj) __attribute__((always_inline)) {
         constexpr int AH = decltype(ahead)::value;
-        if constexpr (AH >= 2) wait_vmcnt<2 * LX>();
-        else if constexpr (AH == 1) wait_vmcnt<LX>();
-        else if constexpr (AH == 0) wait_vmcnt<0>();
+        if constexpr (AH >= 2) wait_vmcnt<2 * LX + WX>();
+        else if constexpr (AH == 1) wait_vmcnt<LX + WX>();
+        else if constexpr (AH == 0) wait_vmcnt<WX>();
         else {  // the first tile: blocks j0 + 1 and j0 + 2 are copied if they exist
             const int ah = min(2, j1 - 1 - j);
-            if (ah >= 2) wait_vmcnt<2 * LX>();
-            else if (ah == 1) wait_vmcnt<LX>();
-            else wait_vmcnt<0>();
+            if (ah >= 2) wait_vmcnt<2 * LX + WX>();
+            else if (ah == 1) wait_vmcnt<LX + WX>();
+            else wait_vmcnt<WX>();
         }
         lds_barrier();  // X(j) in every wave; B written; the last tile's values read
-        if constexpr (!decltype(first)::value) store_slab_rows<C>(out, (int64_t)(j - 1) * C::BN, ep);
+        if constexpr (!APPLY && !decltype(first)::value) store_slab_rows<C>(out, (int64_t)(j - 1) * C::BN, ep);
         zero(acc);
         product(std::true_type{}, lp0, lp1, s0, s1, std::true_type{}, true, acc);
         lds_barrier();  // every wave is done with X(j)
         rows_to_slab_pair<C>(acc, ep, wm, wn, frow, khalf, s0, s1);
         lds_barrier();
-        read_slab_pair<C>(s0, s1, out);
+        if constexpr (APPLY) read_slab_quads<C>(s0, s1, outq);
+        else read_slab_pair<C>(s0, s1, out);
         if constexpr (NEXT_GRAM) product(std::false_type{}, s0, s1, s0, s1, std::false_type{}, false, accg);
         lds_barrier();  // the tile's values are read: the stage takes the next block
+        if constexpr (APPLY) apply_w(j, outq, wv, loadw, wj);
         if constexpr (decltype(copy)::value) copy_x(next, s0, s1);
     };
     using T_ = std::true_type;
@@ -1467,12 +1549,13 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     // rounds of the stages b, c, a while the blocks three tiles on exist, and
     // the R <= 5 tiles left, each count fixed (tail<R>).
     using Two = std::integral_constant<int, 2>;
-    tile(Run{}, T_{}, T_{}, j0, min(j0 + 3, j1 - 1), la0, la1);
+    // W of the next tile likewise (the strip's last again when there is none).
+    tile(Run{}, T_{}, T_{}, j0, min(j0 + 3, j1 - 1), la0, la1, T_{}, min(j0 + 1, j1 - 1));
     int j = j0 + 1;
     for (; j + 5 < j1; j += 3) {
-        tile(Two{}, F_{}, T_{}, j, j + 3, lb0, lb1);
-        tile(Two{}, F_{}, T_{}, j + 1, j + 4, lc0, lc1);
-        tile(Two{}, F_{}, T_{}, j + 2, j + 5, la0, la1);
+        tile(Two{}, F_{}, T_{}, j, j + 3, lb0, lb1, T_{}, j + 1);
+        tile(Two{}, F_{}, T_{}, j + 1, j + 4, lc0, lc1, T_{}, j + 2);
+        tile(Two{}, F_{}, T_{}, j + 2, j + 5, la0, la1, T_{}, j + 3);
     }
     auto tail = [&](auto r) __attribute__((always_inline)) {
         constexpr int R = decltype(r)::value;
@@ -1483,11 +1566,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
         using A1 = std::integral_constant<int, (R - 2 < 2 ? R - 2 : 2)>;
         using A2 = std::integral_constant<int, (R - 3 < 2 ? R - 3 : 2)>;
         using A3 = std::integral_constant<int, (R - 4 < 2 ? R - 4 : 2)>;
-        if constexpr (R > 0) tile(A0{}, F_{}, std::bool_constant<(R > 3)>{}, j, j + 3, lb0, lb1);
-        if constexpr (R > 1) tile(A1{}, F_{}, std::bool_constant<(R > 4)>{}, j + 1, j + 4, lc0, lc1);
-        if constexpr (R > 2) tile(A2{}, F_{}, F_{}, j + 2, 0, la0, la1);
-        if constexpr (R > 3) tile(A3{}, F_{}, F_{}, j + 3, 0, lb0, lb1);
-        if constexpr (R > 4) tile(std::integral_constant<int, 0>{}, F_{}, F_{}, j + 4, 0, lc0, lc1);
+        if constexpr (R > 0)
+            tile(A0{}, F_{}, std::bool_constant<(R > 3)>{}, j, j + 3, lb0, lb1, std::bool_constant<(R > 1)>{}, j + 1);
+        if constexpr (R > 1)
+            tile(A1{}, F_{}, std::bool_constant<(R > 4)>{}, j + 1, j + 4, lc0, lc1, std::bool_constant<(R > 2)>{},
+                 j + 2);
+        if constexpr (R > 2) tile(A2{}, F_{}, F_{}, j + 2, 0, la0, la1, std::bool_constant<(R > 3)>{}, j + 3);
+        if constexpr (R > 3) tile(A3{}, F_{}, F_{}, j + 3, 0, lb0, lb1, std::bool_constant<(R > 4)>{}, j + 4);
+        if constexpr (R > 4) tile(std::integral_constant<int, 0>{}, F_{}, F_{}, j + 4, 0, lc0, lc1, F_{}, 0);
     };
     switch (j1 - j) {
         case 1: tail(std::integral_constant<int, 1>{}); break;
@@ -1499,9 +1585,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
     }
     // every copy has landed (a strip's first tile always copies, for a strip
     // of one tile its own block again) before the band buffer reuses the
-    // first stage and before the workgroup ends
+    // first stage and before the workgroup ends (APPLY: every tile has
+    // stored its W already)
     wait_vmcnt<0>();
-    store_slab_rows<C>(out, (int64_t)(j1 - 1) * C::BN, ep);
+    if constexpr (!APPLY) store_slab_rows<C>(out, (int64_t)(j1 - 1) * C::BN, ep);
     if constexpr (NEXT_GRAM) {
         // this strip's part of the next Gram: raw fp32, as the K-split Gram
         // stores it, through the first stage's first slab (every copy has
@@ -2036,16 +2123,21 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
                                    const XcdSplit& xs, int it, int strip, int next_gram, int stream,
-                                   float a, float b, float c, hipStream_t st) {
+                                   int apply, float a, float b, float c, float decay, float lr,
+                                   hipStream_t st) {
     if (stream) {
         if (next_gram)
-            ns_update_stream_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip,
-                                                                                       xs, it, strip, a, b, c);
+            ns_update_stream_kernel<SmallCfg, true, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
+                d, n, prefix_strip, xs, it, strip, a, b, c, decay, lr);
+        else if (apply)
+            ns_update_stream_kernel<SmallCfg, false, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
+                d, n, prefix_strip, xs, it, strip, a, b, c, decay, lr);
         else
-            ns_update_stream_kernel<SmallCfg, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
-                d, n, prefix_strip, xs, it, strip, a, b, c);
+            ns_update_stream_kernel<SmallCfg, false, false><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(
+                d, n, prefix_strip, xs, it, strip, a, b, c, decay, lr);
         return hipGetLastError();
     }
+    if (apply) return hipErrorInvalidValue;  // only streamed strips apply
     if (next_gram)
         ns_update_strip_kernel<SmallCfg, true><<<xcd_grid(xs), SmallCfg::NT, 0, st>>>(d, n, prefix_strip, xs,
                                                                                       it, strip, a, b, c);

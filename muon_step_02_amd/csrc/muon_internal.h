@@ -100,10 +100,13 @@ hipError_t launch_update_bf16(const MatDesc* d, int n, Prefix p, const XcdSplit&
 // class).  next_gram: each strip also stores its part of the next
 // iteration's K-split Gram (the strip count per matrix equals its gram_split).
 // stream: one workgroup per compute unit streaming its tiles (the class runs
-// alone in the call), else two per compute unit
+// alone in the call), else two per compute unit.  apply (last iteration,
+// stream only, every matrix eligible: ClassPlan::fuse_apply): the strips
+// update W in place, W <- decay W - lr scale X, in place of the apply launch
 hipError_t launch_update_strip_bf16(const MatDesc* d, int n, const int32_t* prefix_strip,
                                    const XcdSplit& xs, int it, int strip, int next_gram, int stream,
-                                   float a, float b, float c, hipStream_t st);
+                                   int apply, float a, float b, float c, float decay, float lr,
+                                   hipStream_t st);
 
 // fp32 class (p.gram == p.tri: the prefix counts every tile of the square).
 // kmax: the largest K of the launch's matrices (n' for the Gram, m' for the

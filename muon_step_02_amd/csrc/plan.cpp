@@ -356,6 +356,7 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
         // equals the split's.
         C.strip = 0;
         C.stream = false;
+        C.fuse_apply = false;
         C.fuse_gram = false;
         C.pstrip.assign(C.count + 1, 0);
         std::vector<int32_t> ts;
@@ -368,6 +369,14 @@ muon_status make_plan(const muon_matrix* mats, int n, const muon_hparams* hp, bo
             if (L >= 2) {
                 C.strip = (int)L;
                 C.stream = alone;
+                C.fuse_apply = alone && need_ptrs;
+                for (int k = 0; k < C.count && C.fuse_apply; ++k) {
+                    const MatDesc& d = P.d[C.first + k];
+                    C.fuse_apply = !d.transposed && d.rows == kClassPad[kSmall] && d.rows == d.mp &&
+                                   d.cols == d.np && d.param_dtype == MUON_F32 && d.vec4 &&
+                                   !d.update_out && !d.qk_smax &&
+                                   ((d.rows - 1) * d.ld_param + d.cols) * 4 < ((int64_t)1 << 31);
+                }
                 ts.resize(C.count);
                 bool split = false, several = false, fits = true, same = true;
                 for (int k = 0; k < C.count; ++k) {

@@ -37,6 +37,11 @@ struct ClassPlan {
     // unit, streamed (and a K-split Gram cut into as many parts as strips);
     // else strips for two workgroups per compute unit
     bool stream = false;
+    // streamed, and every matrix an fp32 weight of exactly 128 rows and a
+    // multiple of 128 columns (not transposed, no padding), rows 16-byte
+    // aligned, without QK-Clip or an update output: the last update applies
+    // the step to W itself and no apply launch runs
+    bool fuse_apply = false;
     int kmax_n = 0, kmax_m = 0;         // largest padded n' and m' of the class
     XcdSplit xs_gram{}, xs_poly{}, xs_upd{};  // bf16 classes: per-XCD tile ranges of equal work
 };

@@ -358,6 +358,19 @@ static void check_plan(const Batch& b, const Plan& P, uintptr_t ws, int cus) {
             const int64_t L = (C.total_upd + slots - 1) / slots;
             EXPECT(C.strip == (L >= 2 ? (int)L : 0));
             EXPECT(C.stream == (C.strip > 0 && alone));
+            {
+                // the strips apply the step themselves only when every matrix
+                // is a plain fp32 weight of 128 x 128k rows
+                bool plain = C.stream;
+                for (int k = 0; k < C.count; ++k) {
+                    const MatDesc& d = P.d[C.first + k];
+                    const muon_matrix& m = b.mats[P.order[C.first + k]];
+                    plain = plain && m.rows == 128 && m.cols % 128 == 0 && m.param_dtype == MUON_F32 &&
+                            !m.update_out && !m.qk_smax && d.vec4 &&
+                            ((m.rows - 1) * m.ld_param + m.cols) * 4 < ((int64_t)1 << 31);
+                }
+                EXPECT(C.fuse_apply == plain);
+            }
             if (C.strip > 0) {
                 int64_t run = 0;
                 EXPECT(C.pstrip.size() == (size_t)C.count + 1 && C.pstrip[0] == 0);
@@ -519,6 +532,7 @@ int main(int argc, char** argv) {
         plan_of(std::vector<std::pair<int64_t, int64_t>>(64, {128, 7168}), P);
         EXPECT(P.cls[kSmall].strip == 14 && P.cls[kSmall].total_strips == 256 && P.cls[kSmall].stream);
         EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram && P.d[0].gram_split == 4);
+        EXPECT(P.cls[kSmall].fuse_apply);  // plain fp32 weights: the last strips apply the step
         // the same blocks beside a 4096^2 matrix: strips of 7 for two
         // workgroups per compute unit, 8 Gram parts, not streamed
         {
@@ -527,7 +541,7 @@ int main(int argc, char** argv) {
             plan_of(sh, P);
             EXPECT(P.cls[kSmall].strip == 7 && P.cls[kSmall].total_strips == 512 && !P.cls[kSmall].stream);
             EXPECT(P.cls[kSmall].gram_split && P.cls[kSmall].fuse_gram);
-            EXPECT(P.d[P.cls[kSmall].first].gram_split == 8);
+            EXPECT(P.d[P.cls[kSmall].first].gram_split == 8 && !P.cls[kSmall].fuse_apply);
         }
         // 16 blocks of 100 x 4900 (39 tiles, 78 slabs each), alone: streamed
         // strips of 3, 13 per block; 13 Gram parts would be shorter than
@@ -535,6 +549,7 @@ int main(int argc, char** argv) {
         plan_of(std::vector<std::pair<int64_t, int64_t>>(16, {100, 4900}), P);
         EXPECT(P.cls[kSmall].strip == 3 && P.cls[kSmall].total_strips == 16 * 13 && P.cls[kSmall].stream);
         EXPECT(P.cls[kSmall].gram_split && !P.cls[kSmall].fuse_gram && P.d[0].gram_split == 9);
+        EXPECT(!P.cls[kSmall].fuse_apply);  // 100 rows: padded, the apply launch runs
         // few small tiles: one tile per workgroup
         plan_of({{128, 4096}, {100, 3000}}, P);
         EXPECT(P.cls[kSmall].strip == 0 && !P.cls[kSmall].fuse_gram && !P.cls[kSmall].stream);

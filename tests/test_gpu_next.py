@@ -372,3 +372,48 @@ def test_streamed_strips_with_fused_gram_parts_are_repeatable():
         res.append([t.clone() for t in Ws + Ms + Os])
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("blocks,tiles,extra,hpd",
+                         [(64, 5, 0, BASE_HP), (32, 36, 0, BASE_HP), (64, 23, 256, BASE_HP),
+                          (64, 23, 0, dict(BASE_HP, steps=1)), (64, 56, 0, dict(BASE_HP, steps=2))],
+                         ids=["strips 2-2-1", "strips 5 x 7 + 1, fused", "ld > cols, fused",
+                              "one iteration", "per-head 128 x 7168, two iterations"])
+def test_streamed_strips_apply_the_step(blocks, tiles, extra, hpd):
+    # Blocks of 128 x 128*tiles fp32 weights (rows of one tensor whose width
+    # may exceed the blocks' by `extra` columns), the small class alone: the
+    # last update's strips update W themselves and no apply launch runs.  The
+    # same blocks with an update output take the apply launch instead; W and
+    # M must agree bit for bit over two carried steps, the untouched columns
+    # stay untouched, and sampled blocks match the oracle.
+    from harness import TOL_BLOCK_BF16, check_output
+    rows, cols = 128, 128 * tiles
+    shape = (rows, cols)
+    sample = sorted({0, 1, blocks // 2, blocks - 1})
+    kw = oracle_kwargs(hpd)
+    Wf = [_weight(blocks * rows, cols + extra, 900 + tiles) for _ in range(2)]
+    Mf = [torch.zeros(blocks * rows, cols + extra, device=DEV) for _ in range(2)]
+    W0_rest = Wf[0][:, cols:].clone()
+    Os = [torch.empty(*shape, device=DEV) for _ in range(blocks)]
+    ref = {b: [f64(Wf[0][b * rows:(b + 1) * rows, :cols]), np.zeros(shape)] for b in sample}
+    for step in range(2):
+        Gf = _grad(blocks * rows, cols + extra, 950 + step)
+        for v in range(2):
+            blk = [(Wf[v][b * rows:(b + 1) * rows, :cols], Gf[b * rows:(b + 1) * rows, :cols],
+                    Mf[v][b * rows:(b + 1) * rows, :cols]) for b in range(blocks)]
+            mats = [mu.muon_matrix(w, g, m, update_out=Os[b] if v == 0 else None)
+                    for b, (w, g, m) in enumerate(blk)]
+            run_muon_step(mats, hp_from(hpd))
+        torch.cuda.synchronize()
+        assert torch.equal(Wf[0], Wf[1]), step
+        assert torch.equal(Mf[0], Mf[1]), step
+        assert torch.equal(Wf[1][:, cols:], W0_rest) and torch.count_nonzero(Mf[1][:, cols:]) == 0
+        for b in sample:
+            sl = slice(b * rows, (b + 1) * rows)
+            W0, M0 = ref[b]
+            Wr, Mr, Or = oracle.muon_matrix_step(W0, f64(Gf[sl, :cols]), M0, **kw)
+            check_output(f64(Os[b]), Or, TOL_O_BF16, TOL_BLOCK_BF16, what="block %d step %d" % (b, step))
+            assert relF(f64(Mf[1][sl, :cols]), Mr) <= TOL_STATE, (step, b)
+            assert relF(f64(Wf[1][sl, :cols]), Wr) <= w_tolerance(kw["lr"], oracle.shape_scale(*shape), Or, Wr,
+                                                                 TOL_O_BF16), (step, b)
+            ref[b] = [f64(Wf[1][sl, :cols]), f64(Mf[1][sl, :cols])]
