@@ -223,7 +223,10 @@ muon_status adamw_step(muon_handle h, const adamw_tensor* ts, int n,
  * kernels compute.  Phases: 0 momentum, 1 norm, 2 gram, 3 poly, 4 update,
  * 5 apply, 6 adamw (matrices whose short side is at most 128, when their
  * update runs in strips, form the polynomial and the later Gram parts inside
- * the update launches: phase 4, with no phase-3 launch for them). */
+ * the update launches: phase 4, with no phase-3 launch for them; when such
+ * matrices are alone in the call and all are fp32 weights of exactly 128 rows
+ * and a multiple of 128 columns, without QK-Clip or update_out, the last
+ * update launch also applies the step and phase 5 records no launch). */
 #define MUON_NUM_PHASES 7
 typedef struct {
     float ms[MUON_NUM_PHASES];     /* summed launch durations per phase */
